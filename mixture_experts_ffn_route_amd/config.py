@@ -1,0 +1,123 @@
+"""Layer configuration and the named synthetic workloads.
+
+Field names follow the model arguments of the "gate-init" excerpt on
+"DeepSeek-V3.2-Exp - Routing weights" and of the V4.1 MoE class on
+"DeepSeek V4.1 - Add shared"; the struct mirrors ``moe_config`` in moe.h.
+"""
+
+from dataclasses import dataclass, field, replace
+
+SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
+ROUTE = {"learned": 0, "hash": 1}
+DTYPE = {"f32": 0, "bf16": 1, "fp4": 2}
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    dim: int
+    n_routed_experts: int
+    n_activated_experts: int
+    moe_inter_dim: int
+    n_expert_groups: int = 1
+    n_limited_groups: int = 1
+    n_shared_experts: int = 1
+    score_func: str = "softmax"
+    route_scale: float = 1.0
+    renormalize: int = -1
+    swiglu_limit: float = 0.0
+    route_mode: str = "learned"
+    vocab_size: int = 0
+    act_dtype: str = "bf16"
+    expert_dtype: str = "bf16"
+    has_bias: bool = False
+
+    @property
+    def renorm(self):
+        if self.renormalize < 0:
+            return self.score_func != "softmax"
+        return bool(self.renormalize)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """A layer config, a token count and the recipe of its synthetic inputs."""
+    name: str
+    cfg: MoEConfig
+    T: int
+    zipf_s: float = 1.1          # hash routing: token frequency p_i ~ i^-s
+    bias_range: float = 0.01     # bias ~ U(-r, r) when cfg.has_bias
+    x_scale: float = 1.0         # x ~ N(0, x_scale^2)
+    seed: int = 0
+    x_rows: int = 0              # draw x with this many rows, keep the first T
+    description: str = ""
+
+
+# The five layer workloads (the small tiny-fp32 one is cheap enough for the
+# oracle at full size; the others are sampled by the parity tests).
+TINY_FP32 = Workload(
+    "tiny_fp32",
+    MoEConfig(dim=128, n_routed_experts=16, n_activated_experts=2, moe_inter_dim=64,
+              score_func="softmax", route_scale=1.0, act_dtype="f32", expert_dtype="f32"),
+    T=64, description="T=64, d=128, 16 experts top-2, softmax, fp32")
+
+HASH_BF16 = Workload(
+    "hash_bf16",
+    MoEConfig(dim=2048, n_routed_experts=64, n_activated_experts=4, moe_inter_dim=1024,
+              route_mode="hash", vocab_size=32768, route_scale=1.0),
+    T=4096, description="hash routing, m=32768 Zipf(1.1), 64 experts top-4, d=2048, I=1024, bf16")
+
+V3_PREFILL = Workload(
+    "v3_prefill",
+    MoEConfig(dim=7168, n_routed_experts=256, n_activated_experts=8, moe_inter_dim=2048,
+              n_expert_groups=8, n_limited_groups=4, score_func="sigmoid", route_scale=2.5,
+              has_bias=True),
+    T=4096, description="DeepSeek-V3 shape prefill, T=4096, d=7168, 256 experts (8 groups, keep 4) top-8")
+
+V3_DECODE = replace(V3_PREFILL, name="v3_decode", T=64, x_rows=4096,
+                    description="DeepSeek-V3 shape decode, T=64 (64 sequences x 1 position)")
+
+V41_FLASH_FP4 = Workload(
+    "v41_flash_fp4",
+    MoEConfig(dim=5120, n_routed_experts=384, n_activated_experts=8, moe_inter_dim=1536,
+              score_func="sqrtsoftplus", route_scale=1.0, swiglu_limit=10.0,
+              expert_dtype="fp4", has_bias=True),
+    T=8192, description="V4.1-Flash shape, T=8192, d=5120, 384 experts top-8, sqrt(softplus), "
+                        "FP4 e2m1 + e8m0/32 routed experts, clamp 10")
+
+FULL_WORKLOADS = {w.name: w for w in (TINY_FP32, HASH_BF16, V3_PREFILL, V3_DECODE, V41_FLASH_FP4)}
+
+# Reduced versions: the same structure at sizes the oracle finishes in
+# seconds while still spanning several GEMM tiles, slabs and a ragged tail.
+SMALL_WORKLOADS = {
+    "tiny_fp32": TINY_FP32,
+    "hash_small": Workload(
+        "hash_small",
+        replace(HASH_BF16.cfg, dim=256, moe_inter_dim=128, n_routed_experts=16, vocab_size=2048),
+        T=301),
+    "v3_small": Workload(
+        "v3_small",
+        replace(V3_PREFILL.cfg, dim=512, moe_inter_dim=256, n_routed_experts=64),
+        T=203),
+    "v3_decode_small": Workload(
+        "v3_decode_small",
+        replace(V3_PREFILL.cfg, dim=512, moe_inter_dim=256, n_routed_experts=64),
+        T=13, x_rows=203),
+    "fp4_small": Workload(
+        "fp4_small",
+        replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48),
+        T=157),
+    "fp4_clamp_small": Workload(
+        "fp4_clamp_small",
+        replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48),
+        T=97, x_scale=20.0),
+    "softmax_groups_nobias": Workload(
+        "softmax_groups_nobias",
+        MoEConfig(dim=256, n_routed_experts=64, n_activated_experts=6, moe_inter_dim=192,
+                  n_expert_groups=4, n_limited_groups=2, score_func="softmax"),
+        T=150),
+    "sigmoid_noshared_big_tiles": Workload(
+        "sigmoid_noshared_big_tiles",
+        MoEConfig(dim=320, n_routed_experts=8, n_activated_experts=2, moe_inter_dim=128,
+                  n_shared_experts=0, score_func="sigmoid", route_scale=1.5, has_bias=True),
+        T=1000),
+}

@@ -1,0 +1,39 @@
+"""Plain CPU oracle for the DeepSeek-style MoE feed-forward layer forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+link anything in this package: only the test suite (``tests/``), the
+``smoke()`` entry of ``__graft_entry__`` and the ``cpu_baseline`` leg of
+``bench.py`` use it.  It shares no code with the HIP library and imports
+nothing from ``mixture_experts_ffn_route_amd``; every input arrives as an
+array argument.
+
+Everything is written for clarity, not speed: float64 NumPy, one token and
+one expert at a time, following the pages' definitions step by step.
+
+Sources (pages, by title and section):
+  * "DeepSeek-V3.2-Exp - Routing weights", excerpts "gate-forward" and
+    "moe-forward" -- the learned gate and the per-expert dispatch loop.
+  * "From One Giant FFN to 384 Tiny Experts", Ch.1 (SwiGLU definition),
+    Ch.4 (DeepSeekMoE gating formula), Ch.6 (selection-only bias),
+    Ch.11.2 (Sqrt(Softplus) affinity), 11.4 (SwiGLU clamp), 11.6 (FP4 experts).
+  * "DeepSeek V4.1 - Add shared" -- the V4.1 MoE class: routed + shared,
+    output cast back to the input dtype.
+  * "How was DeepSeek V4's tid2eid derived?" -- eq. (1)/(2) and the greedy
+    least-loaded construction of the hash-routing table.
+
+Parity status of each function is stated in its module docstring; every
+function here is pinned by a test in ``tests/test_oracle_*.py`` against
+closed forms, brute force, library routines or hand-derived fixtures.
+"""
+
+from .route import affinity, selection_keys, learned_gate, hash_gate
+from .permute import permute
+from .ffn import swiglu_expert, layer_forward, dense_map_forward, fp4_decode, E2M1_VALUES
+from .tid2eid import tid2eid_greedy, tid2eid_objective, tid2eid_bruteforce, balance_violations
+
+__all__ = [
+    "affinity", "selection_keys", "learned_gate", "hash_gate",
+    "permute",
+    "swiglu_expert", "layer_forward", "dense_map_forward", "fp4_decode", "E2M1_VALUES",
+    "tid2eid_greedy", "tid2eid_objective", "tid2eid_bruteforce", "balance_violations",
+]
