@@ -1,0 +1,218 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts feed-forward layer.
+ *
+ * The library computes the forward pass of a DeepSeek-style MoE FFN layer:
+ *
+ *   y[t] = cast( sum_j w[t,j] * FFN_{idx[t,j]}(x[t]) + FFN_shared(x[t]) )
+ *   FFN(u) = W_down( SiLU(min(W_gate u, L)) * clamp(W_up u, -L, L) )
+ *
+ * Sources (pages, by title and section):
+ *   - "DeepSeek-V3.2-Exp - Routing weights": excerpts "gate-init",
+ *     "gate-forward" (learned gate) and "moe-forward" (dispatch loop).
+ *   - "DeepSeek V4.1 - Add shared": the V4.1 MoE class (FP4 routed experts,
+ *     swiglu_limit, shared expert added to every token, y cast to x's dtype).
+ *   - "From One Giant FFN to 384 Tiny Experts": Ch.1 SwiGLU, Ch.4 routed +
+ *     shared formula, Ch.6 selection-only bias, Ch.11.1 hash-routed layers,
+ *     Ch.11.2 Sqrt(Softplus) affinity, Ch.11.4 SwiGLU clamp, Ch.11.6 FP4.
+ *   - "How was DeepSeek V4's tid2eid derived?": eq. (1)-(2) and the greedy
+ *     least-loaded table construction.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns
+ *     every buffer; the library never allocates or frees device memory.
+ *   - GPU work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising.  Outputs are
+ *     valid once the stream reaches that point.
+ *   - Arguments are validated on the host before any launch; invalid ones
+ *     return MOE_ERR_INVALID_ARG (or MOE_ERR_UNSUPPORTED for valid-but-not-
+ *     implemented shapes) and enqueue nothing.  A failed launch returns
+ *     MOE_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Weight matrices are [out, in] row-major with the input (K) dimension
+ *     contiguous, like nn.Linear: gate weight [E, dim]; routed W_gate and
+ *     W_up [E, I, dim]; W_down [E, dim, I]; shared [I, dim], [I, dim], [dim, I].
+ *   - bf16 is IEEE-style bfloat16 (upper half of an fp32); fp32 is IEEE.
+ *   - FP4 routed experts (MOE_DTYPE_FP4_E2M1): E2M1 codes packed two per
+ *     byte along the input dimension, element 2i in the low nibble; one
+ *     E8M0 scale byte (value 2^(e-127)) per 32 consecutive input elements
+ *     of each output row (OCP MXFP4, 1x32 sub-blocks).
+ *   - All calls are thread-safe: the library holds no mutable global state.
+ *     Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* bad pointer, size or config field            */
+  MOE_ERR_UNSUPPORTED = -2,   /* valid config this build does not implement    */
+  MOE_ERR_WORKSPACE = -3,     /* workspace missing, misaligned or too small    */
+  MOE_ERR_HIP = -4            /* a HIP launch or runtime call failed           */
+} moe_status;
+
+typedef enum {                /* affinity s = f(z) of the logits z             */
+  MOE_SCORE_SOFTMAX = 0,      /* softmax over the E routed experts             */
+  MOE_SCORE_SIGMOID = 1,      /* 1 / (1 + exp(-z))                             */
+  MOE_SCORE_SQRTSOFTPLUS = 2  /* sqrt(log(1 + exp(z)))                         */
+} moe_score_func;
+
+typedef enum {
+  MOE_ROUTE_LEARNED = 0,      /* gate GEMM + affinity + bias + group top-k     */
+  MOE_ROUTE_HASH = 1          /* indices = tid2eid[token_id]                   */
+} moe_route_mode;
+
+typedef enum {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1,
+  MOE_DTYPE_FP4_E2M1 = 2      /* routed experts only; see conventions above    */
+} moe_dtype;
+
+/* Layer configuration.  Field names follow the model arguments of the
+ * "gate-init" excerpt and the V4.1 MoE class. */
+typedef struct {
+  int32_t dim;                 /* model width d                                  */
+  int32_t n_routed_experts;    /* E (1..1024; learned routing: 1..512)           */
+  int32_t n_activated_experts; /* k experts per token (1..16, k <= E)            */
+  int32_t n_expert_groups;     /* G (1 = no groups); E % G == 0                  */
+  int32_t n_limited_groups;    /* groups kept per token, 1..G                    */
+  int32_t moe_inter_dim;       /* expert intermediate width I (also the shared) */
+  int32_t n_shared_experts;    /* 0 or 1                                         */
+  int32_t score_func;          /* moe_score_func                                 */
+  float route_scale;           /* weights are multiplied by this                 */
+  int32_t renormalize;         /* -1: renormalise iff score_func != softmax; 0/1 */
+  float swiglu_limit;          /* L > 0 clamps; 0 = no clamp                     */
+  int32_t route_mode;          /* moe_route_mode                                 */
+  int64_t vocab_size;          /* hash routing: rows of tid2eid                  */
+  int32_t act_dtype;           /* x, y, gate weight, shared expert: F32 or BF16  */
+  int32_t expert_dtype;        /* routed experts: F32 (act F32), BF16 or
+                                  FP4_E2M1 (act BF16)                            */
+} moe_config;
+
+/* Layer weights; unused members may be NULL. */
+typedef struct {
+  const void *gate_w;          /* [E, dim] act_dtype (learned routing)           */
+  const float *gate_bias;      /* [E] fp32 selection bias, or NULL               */
+  const void *w_gate;          /* [E, I, dim] (FP4: bytes [E, I, dim/2])         */
+  const void *w_up;            /* [E, I, dim] (FP4: bytes [E, I, dim/2])         */
+  const void *w_down;          /* [E, dim, I] (FP4: bytes [E, dim, I/2])         */
+  const uint8_t *s_gate;       /* FP4 only: E8M0 [E, I, dim/32]                  */
+  const uint8_t *s_up;         /* FP4 only: E8M0 [E, I, dim/32]                  */
+  const uint8_t *s_down;       /* FP4 only: E8M0 [E, dim, I/32]                  */
+  const void *sh_gate;         /* shared expert [I, dim] act_dtype               */
+  const void *sh_up;           /* shared expert [I, dim] act_dtype               */
+  const void *sh_down;         /* shared expert [dim, I] act_dtype               */
+  const int32_t *tid2eid;      /* hash routing: [vocab_size, k] expert ids       */
+} moe_weights;
+
+/* Byte offsets of the sub-buffers moe_forward keeps in its workspace.
+ * Every offset is 256-byte aligned; the workspace base must be too. */
+typedef struct {
+  size_t total_bytes;
+  size_t route_weights;        /* float [T, k]   gate values                     */
+  size_t route_indices;        /* int32 [T, k]   expert ids                      */
+  size_t counts;               /* int32 [E]      pairs per expert                */
+  size_t offsets;              /* int32 [E + 1]  exclusive scan of counts        */
+  size_t sorted_tok;           /* int32 [T*k + T] token of each permuted row;
+                                  rows T*k.. are the shared expert's (row-T*k)   */
+  size_t sorted_slot;          /* int32 [T*k]    slot of each permuted row       */
+  size_t inverse;              /* int32 [T, k]   permuted row of pair (t, j)     */
+  size_t tiles;                /* int32 [max_tiles, 4] GEMM work list           */
+  size_t tile_count;           /* int32 [1]      tiles written by the permute    */
+  size_t flags;                /* uint32 [4]     device error flags (below)      */
+  size_t h;                    /* [T*k + T, I]   SwiGLU activations (bf16/f32)   */
+  size_t yrows;                /* [T*k + T, dim] weighted expert outputs         */
+  int32_t max_tiles;
+  int32_t tile_rows;           /* rows per GEMM tile chosen for this (cfg, T)    */
+} moe_ws_layout;
+
+/* Device error flag bits (flags[0]); a non-zero word means some output rows
+ * were produced from substitute data as described. */
+#define MOE_FLAG_TOKEN_ID_RANGE 1u  /* hash: a token id outside [0, vocab): the
+                                       token used tid2eid row 0 with weight 0   */
+#define MOE_FLAG_EXPERT_RANGE   2u  /* permute: an expert id outside [0, E):
+                                       that pair was dropped (inverse = -1)     */
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_string(int status);
+
+/* Host-only check of a configuration (no GPU needed).  Returns MOE_OK,
+ * MOE_ERR_INVALID_ARG for inconsistent fields (E % G, k > E,
+ * n_limited_groups > G, k > n_limited_groups * E / G, bad enums, ...) or
+ * MOE_ERR_UNSUPPORTED for shapes this build does not implement (bf16/FP4
+ * paths need dim % 64 == 0 and I % 64 == 0, FP4 dim % 128 == 0 and
+ * I % 128 == 0; group ranges whose size over
+ * ceil(E/64) is not a power of two). */
+int moe_validate_config(const moe_config *cfg);
+
+/* Greedy hash-routing table ("How was DeepSeek V4's tid2eid derived?",
+ * section "Mathematical formulation" and its reference implementation).
+ * Tokens are taken by decreasing p (equal p: ascending id); each gets the k
+ * experts of smallest current load (equal loads: ascending expert id), stored
+ * in ascending (load, id) order, and each of those loads grows by p_i / k.
+ *   p        (host) [m] token frequencies, any order, non-negative
+ *   tid2eid  (host) [m, k] output, row = token id
+ *   load     (host) [n] final normalised loads f, or NULL
+ *   max_vio, min_vio (host) max(f) * n - 1 and min(f) * n - 1, or NULL
+ * Pure host code, O(m * n); returns MOE_ERR_INVALID_ARG for m < 1, n < 1,
+ * k < 1, k > n, NULL p/tid2eid or a negative/NaN p. */
+int moe_build_tid2eid(const double *p, int64_t m, int32_t n, int32_t k,
+                      int32_t *tid2eid, double *load,
+                      double *max_vio, double *min_vio);
+
+/* Workspace needed by moe_forward for T tokens, and where each part lives.
+ * Host-only; layout may be NULL.  Returns MOE_OK or a validation error. */
+int moe_workspace_layout(const moe_config *cfg, int64_t T,
+                         moe_ws_layout *layout);
+size_t moe_workspace_size(const moe_config *cfg, int64_t T); /* 0 if invalid */
+
+/* Routing ("gate-forward" excerpt; hash rule of Ch.11.1).
+ *   x         [T, dim] act_dtype (learned routing; may be NULL for hash)
+ *   token_ids [T] int32 (hash routing; ignored for learned)
+ *   weights   [T, k] float out: gate values (hash: route_scale / k)
+ *   indices   [T, k] int32 out: expert ids, in descending biased-score
+ *             order; equal scores go to the lower expert id
+ * The score GEMM, affinity, bias, group limit, top-k and renormalisation run
+ * in one kernel; logits never leave the chip. */
+int moe_route(const moe_config *cfg, const moe_weights *w, const void *x,
+              const int32_t *token_ids, int64_t T,
+              float *weights, int32_t *indices, void *stream);
+
+/* Permutation by expert (the bincount / where loop of "moe-forward").
+ *   indices     [T, k] int32 expert ids
+ *   counts      [E]    out: pairs per expert
+ *   offsets     [E+1]  out: exclusive scan, offsets[E] = pairs kept
+ *   sorted_tok  [T*k]  out: token of each permuted row
+ *   sorted_slot [T*k]  out: slot of each permuted row
+ *   inverse     [T, k] out: permuted row of each pair (-1 if dropped)
+ * Rows of one expert are in ascending (token, slot) order, so the result is
+ * deterministic.  Ids outside [0, E) are dropped and flagged in `flags`
+ * (uint32 [4], may be NULL; the caller zeroes it beforehand). */
+int moe_permute(const moe_config *cfg, const int32_t *indices, int64_t T,
+                int32_t *counts, int32_t *offsets, int32_t *sorted_tok,
+                int32_t *sorted_slot, int32_t *inverse, uint32_t *flags,
+                void *stream);
+
+/* Full layer forward: route -> permute -> grouped GEMM1 (gate|up + SwiGLU,
+ * clamp) -> grouped GEMM2 (down, times the gate value) -> combine with the
+ * shared expert.  No host synchronisation inside.
+ *   x   [T, dim] act_dtype;  token_ids [T] int32 (hash routing only)
+ *   y   [T, dim] act_dtype out (may not alias x)
+ *   ws  device workspace of at least moe_workspace_size(cfg, T) bytes,
+ *       256-byte aligned; its sub-buffers (moe_ws_layout) hold the
+ *       routing, permutation and intermediates of this call afterwards.
+ * T == 0 is a no-op.  MOE_ERR_WORKSPACE if ws is NULL, misaligned or small. */
+int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
+                const int32_t *token_ids, int64_t T, void *y,
+                void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,216 @@
+"""Thin Python binding of the C ABI in include/moe.h (argument marshalling only).
+
+Every function has the name of the C entry point it calls.  Device buffers
+are torch tensors (PyTorch provides the device memory and the stream); all
+arithmetic happens in the HIP library.  There is no fallback: if the library
+is not built, importing this module raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # loaded first so the library binds to the same HIP runtime as torch
+
+from .config import DTYPE, ROUTE, SCORE, MoEConfig
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+MOE_FLAG_TOKEN_ID_RANGE = 1
+MOE_FLAG_EXPERT_RANGE = 2
+
+EXPORTED_SYMBOLS = (
+    "moe_status_string", "moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout",
+    "moe_workspace_size", "moe_route", "moe_permute", "moe_forward",
+)
+
+
+class MoeConfigC(ctypes.Structure):
+    _fields_ = [
+        ("dim", ctypes.c_int32), ("n_routed_experts", ctypes.c_int32),
+        ("n_activated_experts", ctypes.c_int32), ("n_expert_groups", ctypes.c_int32),
+        ("n_limited_groups", ctypes.c_int32), ("moe_inter_dim", ctypes.c_int32),
+        ("n_shared_experts", ctypes.c_int32), ("score_func", ctypes.c_int32),
+        ("route_scale", ctypes.c_float), ("renormalize", ctypes.c_int32),
+        ("swiglu_limit", ctypes.c_float), ("route_mode", ctypes.c_int32),
+        ("vocab_size", ctypes.c_int64), ("act_dtype", ctypes.c_int32),
+        ("expert_dtype", ctypes.c_int32),
+    ]
+
+
+class MoeWeightsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "gate_w", "gate_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+        "sh_gate", "sh_up", "sh_down", "tid2eid")]
+
+
+class MoeWsLayoutC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "total_bytes", "route_weights", "route_indices", "counts", "offsets", "sorted_tok",
+        "sorted_slot", "inverse", "tiles", "tile_count", "flags", "h", "yrows")] + [
+        ("max_tiles", ctypes.c_int32), ("tile_rows", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    cfgp, wp = ctypes.POINTER(MoeConfigC), ctypes.POINTER(MoeWeightsC)
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_validate_config.argtypes = [cfgp]
+    lib.moe_build_tid2eid.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
+    lib.moe_workspace_layout.argtypes = [cfgp, i64, ctypes.POINTER(MoeWsLayoutC)]
+    lib.moe_workspace_size.restype = ctypes.c_size_t
+    lib.moe_workspace_size.argtypes = [cfgp, i64]
+    lib.moe_route.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, vp]
+    lib.moe_permute.argtypes = [cfgp, vp, i64, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_forward.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]
+    for f in ("moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout", "moe_route",
+              "moe_permute", "moe_forward"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_string(status)} ({status})")
+
+
+def _check(status, where):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        return ctypes.c_void_p(t.data_ptr())
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data_as(ctypes.c_void_p)
+    raise TypeError(type(t))
+
+
+def _stream(stream):
+    if isinstance(stream, int):              # a raw hipStream_t (0 = default stream)
+        return ctypes.c_void_p(stream)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def config_c(cfg: MoEConfig) -> MoeConfigC:
+    return MoeConfigC(
+        cfg.dim, cfg.n_routed_experts, cfg.n_activated_experts, cfg.n_expert_groups,
+        cfg.n_limited_groups, cfg.moe_inter_dim, cfg.n_shared_experts, SCORE[cfg.score_func],
+        cfg.route_scale, cfg.renormalize, cfg.swiglu_limit, ROUTE[cfg.route_mode],
+        cfg.vocab_size, DTYPE[cfg.act_dtype], DTYPE[cfg.expert_dtype])
+
+
+def weights_c(layer: dict) -> MoeWeightsC:
+    return MoeWeightsC(*[_ptr(layer.get(n)) for n in (
+        "gate_w", "gate_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+        "sh_gate", "sh_up", "sh_down", "tid2eid")])
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(int(status)).decode()
+
+
+def moe_validate_config(cfg: MoEConfig) -> int:
+    return _lib.moe_validate_config(ctypes.byref(config_c(cfg)))
+
+
+def moe_build_tid2eid(p, n: int, k: int):
+    """Greedy table on the host.  Returns (tid2eid int32 [m,k], load [n], max_vio, min_vio)."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    m = p.shape[0]
+    table = np.empty((m, k), dtype=np.int32)
+    load = np.empty(n, dtype=np.float64)
+    mx, mn = ctypes.c_double(), ctypes.c_double()
+    _check(_lib.moe_build_tid2eid(_ptr(p), m, n, k, _ptr(table), _ptr(load), ctypes.byref(mx),
+                                  ctypes.byref(mn)), "moe_build_tid2eid")
+    return table, load, mx.value, mn.value
+
+
+def moe_workspace_layout(cfg: MoEConfig, T: int) -> dict:
+    lay = MoeWsLayoutC()
+    _check(_lib.moe_workspace_layout(ctypes.byref(config_c(cfg)), T, ctypes.byref(lay)),
+           "moe_workspace_layout")
+    return {name: getattr(lay, name) for name, _ in MoeWsLayoutC._fields_}
+
+
+def moe_workspace_size(cfg: MoEConfig, T: int) -> int:
+    return _lib.moe_workspace_size(ctypes.byref(config_c(cfg)), T)
+
+
+def moe_route(cfg: MoEConfig, layer: dict, x, token_ids, T: int, weights, indices, stream=None):
+    _check(_lib.moe_route(ctypes.byref(config_c(cfg)), ctypes.byref(weights_c(layer)), _ptr(x),
+                          _ptr(token_ids), T, _ptr(weights), _ptr(indices), _stream(stream)),
+           "moe_route")
+
+
+def moe_permute(cfg: MoEConfig, indices, T: int, counts, offsets, sorted_tok, sorted_slot,
+                inverse, flags=None, stream=None):
+    _check(_lib.moe_permute(ctypes.byref(config_c(cfg)), _ptr(indices), T, _ptr(counts),
+                            _ptr(offsets), _ptr(sorted_tok), _ptr(sorted_slot), _ptr(inverse),
+                            _ptr(flags), _stream(stream)), "moe_permute")
+
+
+def moe_forward(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, ws, stream=None,
+                ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.moe_forward(ctypes.byref(config_c(cfg)), ctypes.byref(weights_c(layer)), _ptr(x),
+                            _ptr(token_ids), T, _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_forward")
+
+
+# ---------------------------------------------------------------------------
+# Convenience views of a forward workspace (no computation).
+
+def alloc_workspace(cfg: MoEConfig, T: int, device="cuda"):
+    size = moe_workspace_size(cfg, T)
+    if size == 0:
+        raise MoEError(moe_validate_config(cfg), "moe_workspace_size")
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(size, dtype=torch.uint8, device=device)
+
+
+def workspace_views(cfg: MoEConfig, T: int, ws):
+    """Typed views of the routing, permutation and intermediate buffers."""
+    lay = moe_workspace_layout(cfg, T)
+    k, E = cfg.n_activated_experts, cfg.n_routed_experts
+    rows = T * k + T * cfg.n_shared_experts
+    edt = torch.float32 if cfg.act_dtype == "f32" else torch.bfloat16
+
+    def view(off, n, dtype):
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return ws[off:off + nbytes].view(dtype)
+
+    return {
+        "route_weights": view(lay["route_weights"], T * k, torch.float32).view(T, k),
+        "route_indices": view(lay["route_indices"], T * k, torch.int32).view(T, k),
+        "counts": view(lay["counts"], E, torch.int32),
+        "offsets": view(lay["offsets"], E + 1, torch.int32),
+        "sorted_tok": view(lay["sorted_tok"], T * k + T, torch.int32),
+        "sorted_slot": view(lay["sorted_slot"], T * k, torch.int32),
+        "inverse": view(lay["inverse"], T * k, torch.int32).view(T, k),
+        "tiles": view(lay["tiles"], 4 * lay["max_tiles"], torch.int32).view(-1, 4),
+        "tile_count": view(lay["tile_count"], 1, torch.int32),
+        "flags": view(lay["flags"], 4, torch.int32),
+        "h": view(lay["h"], rows * cfg.moe_inter_dim, edt).view(rows, cfg.moe_inter_dim),
+        "yrows": view(lay["yrows"], rows * cfg.dim, edt).view(rows, cfg.dim),
+        "layout": lay,
+    }

@@ -1,0 +1,60 @@
+// Host-side launch interface between the C ABI (moe_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Learned routing: fused score GEMM + affinity + bias + group limit + top-k.
+hipError_t launch_route_learned(const moe_config &cfg, const void *x, const void *gate_w,
+                                const float *bias, int64_t T, float *weights,
+                                int32_t *indices, hipStream_t s);
+
+// Hash routing: indices = tid2eid[token_id], weights = route_scale / k.
+hipError_t launch_route_hash(const moe_config &cfg, const int32_t *token_ids,
+                             const int32_t *tid2eid, int64_t T, float *weights,
+                             int32_t *indices, uint32_t *flags, hipStream_t s);
+
+// Work list for the grouped GEMMs, written by the permute kernel.
+struct TileSpec {
+  int32_t *tiles;        // [max_tiles, 4]: group, first row, rows, 0
+  int32_t *tile_count;   // [1]
+  int tile_rows;         // rows per tile (BM)
+  int n_shared_tiles;    // shared-expert tiles, stored first
+  int32_t *shared_rows_tok;  // sorted_tok + T*k: identity rows for the shared expert
+};
+
+hipError_t launch_permute(int E, int k, int64_t T, const int32_t *indices, int32_t *counts,
+                          int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,
+                          int32_t *inverse, uint32_t *flags, const TileSpec *tiles,
+                          bool clear_flags, hipStream_t s);
+
+hipError_t launch_clear_flags(uint32_t *flags, hipStream_t s);
+
+// Everything the expert GEMMs and the combine need for one forward call.
+struct ExpertPlan {
+  int64_t T;
+  int k, E, dim, inter;
+  bool has_shared;
+  float swiglu_limit;
+  int act_dtype, expert_dtype;
+  const void *x;
+  const moe_weights *w;
+  const float *route_w;
+  const int32_t *route_idx, *offsets;
+  const int32_t *sorted_tok, *sorted_slot, *inverse;
+  const int32_t *tiles, *tile_count;
+  int max_tiles, tile_rows, n_shared_tiles;
+  void *h, *yrows, *y;
+};
+
+// Rows per GEMM tile chosen for a layer of T tokens (depends on the
+// expected rows per expert, T*k/E).
+int choose_tile_rows(const moe_config &cfg, int64_t T);
+
+hipError_t launch_experts(const ExpertPlan &p, hipStream_t s);
+
+}  // namespace moe

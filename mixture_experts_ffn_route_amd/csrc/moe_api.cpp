@@ -1,0 +1,292 @@
+// C ABI of the MoE layer library: validation, workspace layout, the host
+// tid2eid builder and the launch sequence of a forward pass.  See moe.h for
+// the contract of each entry point.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "internal.h"
+#include "moe.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int validate(const moe_config *c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  const int E = c->n_routed_experts, k = c->n_activated_experts, G = c->n_expert_groups;
+  if (c->dim < 1 || E < 1 || k < 1 || c->moe_inter_dim < 1) return MOE_ERR_INVALID_ARG;
+  if (k > E) return MOE_ERR_INVALID_ARG;
+  if (G < 1 || E % G != 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_limited_groups < 1 || c->n_limited_groups > G) return MOE_ERR_INVALID_ARG;
+  if (G > 1 && (int64_t)k > (int64_t)c->n_limited_groups * (E / G)) return MOE_ERR_INVALID_ARG;
+  if (c->score_func < MOE_SCORE_SOFTMAX || c->score_func > MOE_SCORE_SQRTSOFTPLUS)
+    return MOE_ERR_INVALID_ARG;
+  if (c->route_mode != MOE_ROUTE_LEARNED && c->route_mode != MOE_ROUTE_HASH)
+    return MOE_ERR_INVALID_ARG;
+  if (c->renormalize < -1 || c->renormalize > 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->route_scale)) return MOE_ERR_INVALID_ARG;
+  if (!(c->swiglu_limit >= 0.f) || std::isinf(c->swiglu_limit)) return MOE_ERR_INVALID_ARG;
+  if (c->n_shared_experts < 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_shared_experts > 1) return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == MOE_DTYPE_F32) {
+    if (c->expert_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
+  } else if (c->act_dtype == MOE_DTYPE_BF16) {
+    if (c->expert_dtype != MOE_DTYPE_BF16 && c->expert_dtype != MOE_DTYPE_FP4_E2M1)
+      return MOE_ERR_INVALID_ARG;
+    if (c->dim % 64 != 0 || c->moe_inter_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    // FP4 weights are consumed 128 inputs (four 32-blocks) per stage
+    if (c->expert_dtype == MOE_DTYPE_FP4_E2M1 && (c->dim % 128 != 0 || c->moe_inter_dim % 128 != 0))
+      return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (k > 16 || E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (c->route_mode == MOE_ROUTE_HASH) {
+    if (c->vocab_size < 1) return MOE_ERR_INVALID_ARG;
+  } else {
+    if (E > 512) return MOE_ERR_UNSUPPORTED;
+    if (G > 1) {
+      const int epl = (E + 63) / 64;
+      const int gs = E / G;
+      if (G > 64 || gs % epl != 0 || !is_pow2(gs / epl)) return MOE_ERR_UNSUPPORTED;
+    }
+  }
+  return MOE_OK;
+}
+
+int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
+  const int st = validate(c);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t k = c->n_activated_experts, E = c->n_routed_experts;
+  const int64_t shared = c->n_shared_experts;
+  const int64_t rows = T * k + T * shared;
+  if (T * (k + 1) > INT32_MAX - 1) return MOE_ERR_UNSUPPORTED;
+  const int bm = moe::choose_tile_rows(*c, T);
+  const int64_t n_sh = shared ? (T + bm - 1) / bm : 0;
+  const int64_t max_tiles = n_sh + (T * k + bm - 1) / bm + std::min<int64_t>(E, T * k);
+  const size_t es = c->act_dtype == MOE_DTYPE_F32 ? 4 : 2;
+  moe_ws_layout l;
+  std::memset(&l, 0, sizeof(l));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  l.route_weights = take(sizeof(float) * T * k);
+  l.route_indices = take(sizeof(int32_t) * T * k);
+  l.counts = take(sizeof(int32_t) * E);
+  l.offsets = take(sizeof(int32_t) * (E + 1));
+  l.sorted_tok = take(sizeof(int32_t) * (T * k + T));
+  l.sorted_slot = take(sizeof(int32_t) * T * k);
+  l.inverse = take(sizeof(int32_t) * T * k);
+  l.tiles = take(sizeof(int32_t) * 4 * max_tiles);
+  l.tile_count = take(sizeof(int32_t));
+  l.flags = take(sizeof(uint32_t) * 4);
+  l.h = take(es * rows * c->moe_inter_dim);
+  l.yrows = take(es * rows * c->dim);
+  l.total_bytes = off;
+  l.max_tiles = (int32_t)max_tiles;
+  l.tile_rows = bm;
+  if (out) *out = l;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int moe_validate_config(const moe_config *cfg) { return validate(cfg); }
+
+int moe_build_tid2eid(const double *p, int64_t m, int32_t n, int32_t k, int32_t *tid2eid,
+                      double *load, double *max_vio, double *min_vio) {
+  if (!p || !tid2eid || m < 1 || n < 1 || k < 1 || k > n) return MOE_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < m; ++i)
+    if (!(p[i] >= 0.0) || std::isinf(p[i])) return MOE_ERR_INVALID_ARG;
+  // tokens by decreasing frequency, equal frequencies by ascending id
+  std::vector<int64_t> order(m);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [p](int64_t a, int64_t b) { return p[a] > p[b]; });
+  std::vector<double> f(n, 0.0);
+  std::vector<int32_t> pick(k);
+  for (int64_t i : order) {
+    // k smallest (load, id) pairs, kept sorted ascending by insertion
+    int have = 0;
+    for (int32_t j = 0; j < n; ++j) {
+      const double fj = f[j];
+      if (have == k && !(fj < f[pick[k - 1]])) continue;   // ids ascend: equal load loses
+      int pos = have < k ? have : k - 1;
+      while (pos > 0 && fj < f[pick[pos - 1]]) {
+        pick[pos] = pick[pos - 1];
+        --pos;
+      }
+      pick[pos] = j;
+      if (have < k) ++have;
+    }
+    const double share = p[i] / (double)k;
+    for (int q = 0; q < k; ++q) {
+      f[pick[q]] += share;
+      tid2eid[i * k + q] = pick[q];
+    }
+  }
+  double mx = f[0], mn = f[0];
+  for (int32_t j = 1; j < n; ++j) {
+    mx = std::max(mx, f[j]);
+    mn = std::min(mn, f[j]);
+  }
+  if (load) std::copy(f.begin(), f.end(), load);
+  if (max_vio) *max_vio = mx * n - 1.0;
+  if (min_vio) *min_vio = mn * n - 1.0;
+  return MOE_OK;
+}
+
+int moe_workspace_layout(const moe_config *cfg, int64_t T, moe_ws_layout *layout) {
+  return make_layout(cfg, T, layout);
+}
+
+size_t moe_workspace_size(const moe_config *cfg, int64_t T) {
+  moe_ws_layout l;
+  return make_layout(cfg, T, &l) == MOE_OK ? l.total_bytes : 0;
+}
+
+int moe_route(const moe_config *cfg, const moe_weights *w, const void *x,
+              const int32_t *token_ids, int64_t T, float *weights, int32_t *indices,
+              void *stream) {
+  int st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (!w || T < 0 || (T > 0 && (!weights || !indices))) return MOE_ERR_INVALID_ARG;
+  if (T * cfg->n_activated_experts > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (cfg->route_mode == MOE_ROUTE_HASH) {
+    if (!token_ids || !w->tid2eid) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, weights, indices,
+                                             nullptr, s));
+  }
+  if (!x || !w->gate_w) return MOE_ERR_INVALID_ARG;
+  return hip_status(
+      moe::launch_route_learned(*cfg, x, w->gate_w, w->gate_bias, T, weights, indices, s));
+}
+
+int moe_permute(const moe_config *cfg, const int32_t *indices, int64_t T, int32_t *counts,
+                int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot, int32_t *inverse,
+                uint32_t *flags, void *stream) {
+  int st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0 || !counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!indices || !sorted_tok || !sorted_slot || !inverse)) return MOE_ERR_INVALID_ARG;
+  if (T * cfg->n_activated_experts > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_permute(cfg->n_routed_experts, cfg->n_activated_experts, T,
+                                        indices, counts, offsets, sorted_tok, sorted_slot,
+                                        inverse, flags, nullptr, false, (hipStream_t)stream));
+}
+
+int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
+                const int32_t *token_ids, int64_t T, void *y, void *ws, size_t ws_bytes,
+                void *stream) {
+  moe_ws_layout L;
+  int st = make_layout(cfg, T, &L);
+  if (st != MOE_OK) return st;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !y || x == y) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+  if (cfg->expert_dtype == MOE_DTYPE_FP4_E2M1 && (!w->s_gate || !w->s_up || !w->s_down))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared_experts == 1 && (!w->sh_gate || !w->sh_up || !w->sh_down))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->route_mode == MOE_ROUTE_HASH) {
+    if (!token_ids || !w->tid2eid) return MOE_ERR_INVALID_ARG;
+  } else if (!w->gate_w) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (!ws || ((uintptr_t)ws % kAlign) != 0 || ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)ws;
+  float *route_w = (float *)(base + L.route_weights);
+  int32_t *route_idx = (int32_t *)(base + L.route_indices);
+  int32_t *counts = (int32_t *)(base + L.counts);
+  int32_t *offsets = (int32_t *)(base + L.offsets);
+  int32_t *sorted_tok = (int32_t *)(base + L.sorted_tok);
+  int32_t *sorted_slot = (int32_t *)(base + L.sorted_slot);
+  int32_t *inverse = (int32_t *)(base + L.inverse);
+  int32_t *tiles = (int32_t *)(base + L.tiles);
+  int32_t *tile_count = (int32_t *)(base + L.tile_count);
+  uint32_t *flags = (uint32_t *)(base + L.flags);
+  const int k = cfg->n_activated_experts;
+  const bool hash = cfg->route_mode == MOE_ROUTE_HASH;
+
+  hipError_t e;
+  if (hash) {
+    if ((e = moe::launch_clear_flags(flags, s)) != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, route_w, route_idx, flags, s);
+  } else {
+    e = moe::launch_route_learned(*cfg, x, w->gate_w, w->gate_bias, T, route_w, route_idx, s);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  moe::TileSpec ts;
+  ts.tiles = tiles;
+  ts.tile_count = tile_count;
+  ts.tile_rows = L.tile_rows;
+  ts.n_shared_tiles = cfg->n_shared_experts ? (int)((T + L.tile_rows - 1) / L.tile_rows) : 0;
+  ts.shared_rows_tok = sorted_tok + T * k;
+  e = moe::launch_permute(cfg->n_routed_experts, k, T, route_idx, counts, offsets, sorted_tok,
+                          sorted_slot, inverse, flags, &ts, /*clear_flags=*/!hash, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  moe::ExpertPlan p;
+  p.T = T;
+  p.k = k;
+  p.E = cfg->n_routed_experts;
+  p.dim = cfg->dim;
+  p.inter = cfg->moe_inter_dim;
+  p.has_shared = cfg->n_shared_experts == 1;
+  p.swiglu_limit = cfg->swiglu_limit;
+  p.act_dtype = cfg->act_dtype;
+  p.expert_dtype = cfg->expert_dtype;
+  p.x = x;
+  p.w = w;
+  p.route_w = route_w;
+  p.route_idx = route_idx;
+  p.offsets = offsets;
+  p.sorted_tok = sorted_tok;
+  p.sorted_slot = sorted_slot;
+  p.inverse = inverse;
+  p.tiles = tiles;
+  p.tile_count = tile_count;
+  p.max_tiles = L.max_tiles;
+  p.tile_rows = L.tile_rows;
+  p.n_shared_tiles = ts.n_shared_tiles;
+  p.h = base + L.h;
+  p.yrows = base + L.yrows;
+  p.y = y;
+  return hip_status(moe::launch_experts(p, s));
+}
+
+}  // extern "C"

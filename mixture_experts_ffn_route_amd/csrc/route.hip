@@ -1,0 +1,332 @@
+// Routing kernels for gfx950.
+//
+// Learned gate ("DeepSeek-V3.2-Exp - Routing weights", excerpt "gate-forward";
+// affinities from "From One Giant FFN to 384 Tiny Experts" Ch.4, Ch.7 and
+// Ch.11.2; the selection-only bias of Ch.6): one workgroup owns a block of
+// tokens and all E experts.  Phase 1 computes the fp32 logits z = x . W^T
+// (bf16 operands on MFMA 16x16x32 with fp32 accumulation, or fp32 FMAs for
+// fp32 layers) and parks them in LDS.  Phase 2 gives each token to one
+// wavefront: lane l holds experts l*EPL .. l*EPL+EPL-1 in registers, applies
+// the affinity and bias, reduces group top-2 sums with lane exchanges, ranks
+// the groups, and runs k rounds of a wave-wide arg-max (ties to the lower
+// expert id).  Only the k (index, weight) pairs per token reach HBM.
+//
+// Hash gate (Ch.11.1; "How was DeepSeek V4's tid2eid derived?"): a gather of
+// tid2eid rows with uniform weights.
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+struct RouteArgs {
+  const void *x;        // [T, d] bf16 or f32
+  const void *w;        // [E, d] same dtype
+  const float *bias;    // [E] or null
+  int64_t T;
+  int d, E, k, G, topk_groups, score_func, renorm;
+  float route_scale;
+  float *weights;       // [T, k]
+  int32_t *indices;     // [T, k]
+};
+
+// ---------------------------------------------------------------------------
+// Phase 2: selection for one token held by one wavefront.
+// zrow: the token's E logits in LDS.  EPL experts per lane.
+template <int EPL>
+__device__ __forceinline__ void select_token(const RouteArgs &a, const float *zrow, int64_t t,
+                                             int lane) {
+  float s[EPL], key[EPL];
+  const int E = a.E;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane * EPL + j;
+    s[j] = (e < E) ? zrow[e] : -INFINITY;
+  }
+  // affinity
+  if (a.score_func == MOE_SCORE_SOFTMAX) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) m = fmaxf(m, s[j]);
+    m = wave_max(m);
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane * EPL + j;
+      s[j] = (e < E) ? expf(s[j] - m) : 0.f;
+      part += s[j];
+    }
+    const float inv = 1.f / wave_sum(part);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) s[j] *= inv;
+  } else if (a.score_func == MOE_SCORE_SIGMOID) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) s[j] = 1.f / (1.f + expf(-s[j]));
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const float z = s[j];
+      s[j] = sqrtf(fmaxf(z, 0.f) + log1pf(expf(-fabsf(z))));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane * EPL + j;
+    key[j] = (e < E) ? (a.bias ? s[j] + a.bias[e] : s[j]) : -INFINITY;
+  }
+
+  // group limit: lanes_per_group is a power of two (checked on the host)
+  if (a.G > 1) {
+    const int lpg = (E / a.G) / EPL;
+    float a1 = -INFINITY, a2 = -INFINITY;   // largest and second largest key
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const float v = key[j];
+      if (v > a1) { a2 = a1; a1 = v; } else if (v > a2) { a2 = v; }
+    }
+    // merge (a1, a2) pairs across the lpg lanes of the group
+#define MOE_GROUP_MERGE(M)                                              \
+    if (lpg > M) {                                                      \
+      const float b1 = xor_lane<M>(a1), b2 = xor_lane<M>(a2);           \
+      const float hi = fmaxf(a1, b1), lo = fminf(a1, b1);               \
+      a2 = fmaxf(lo, fmaxf(a2, b2));                                    \
+      a1 = hi;                                                          \
+    }
+    MOE_GROUP_MERGE(1) MOE_GROUP_MERGE(2) MOE_GROUP_MERGE(4)
+    MOE_GROUP_MERGE(8) MOE_GROUP_MERGE(16) MOE_GROUP_MERGE(32)
+#undef MOE_GROUP_MERGE
+    const float gs = a.bias ? (a1 + a2) : a1;
+    const int g = lane / lpg;
+    int rank = 0;
+    for (int gg = 0; gg < a.G; ++gg) {
+      const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs), gg * lpg));
+      rank += (v > gs) || (v == gs && gg < g);
+    }
+    if (g >= a.G || rank >= a.topk_groups) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) key[j] = -INFINITY;
+    }
+  }
+
+  // top-k: k rounds of a wave-wide arg-max over (key desc, expert id asc)
+  unsigned taken = 0;
+  int my_idx = 0;
+  float my_s = 0.f, ssum = 0.f;
+  for (int r = 0; r < a.k; ++r) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {   // j ascending = expert id ascending: ties keep the lower id
+      const int e = lane * EPL + j;
+      const bool cand = !((taken >> j) & 1u) && e < E;
+      if (cand && (be == 0x7fffffff || key[j] > bv)) { bv = key[j]; be = e; }
+    }
+#define MOE_ARGMAX_STEP(M)                                                   \
+    {                                                                        \
+      const float ov = xor_lane<M>(bv);                                      \
+      const int oe = xor_lane<M>(be);                                        \
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }            \
+    }
+    MOE_ARGMAX_STEP(1) MOE_ARGMAX_STEP(2) MOE_ARGMAX_STEP(4)
+    MOE_ARGMAX_STEP(8) MOE_ARGMAX_STEP(16) MOE_ARGMAX_STEP(32)
+#undef MOE_ARGMAX_STEP
+    const int owner = be / EPL;
+    const int slot = be - owner * EPL;
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) if (j == slot) mine = s[j];
+    if (lane == owner) taken |= 1u << slot;
+    const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), owner));
+    if (lane == r) { my_idx = be; my_s = sv; }
+    ssum += sv;
+  }
+  if (lane < a.k) {
+    float w = my_s;
+    if (a.renorm) w = w / ssum;
+    w *= a.route_scale;
+    a.indices[t * a.k + lane] = my_idx;
+    a.weights[t * a.k + lane] = w;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 layers: logits on MFMA.  MT 16-token row blocks per workgroup; the E
+// experts are cut into 16-wide column blocks, wave w owning blocks w, w+4, ...
+// (EPL = ceil(E/64) of them, the same count as experts per lane in phase 2).
+template <int EPL, int MT>
+__global__ __launch_bounds__(256) void route_learned_bf16(const RouteArgs a) {
+  constexpr int BT = 16 * MT;
+  extern __shared__ float zl[];                 // [BT][E + 1]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
+  const int E = a.E, d = a.d, ldz = E + 1;
+  const bf16 *x = (const bf16 *)a.x;
+  const bf16 *w = (const bf16 *)a.w;
+
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const bf16 *xrow[MT];
+  bool xok[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t t = t0 + m * 16 + r16;
+    xok[m] = t < a.T;
+    xrow[m] = x + (xok[m] ? t : 0) * (int64_t)d + kq;
+  }
+  const bf16 *wrow[EPL];
+  bool wok[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = (wave + 4 * j) * 16 + r16;
+    wok[j] = e < E;
+    wrow[j] = w + (int64_t)(wok[j] ? e : 0) * d + kq;
+  }
+  f32x4 acc[MT][EPL];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16x8 zero8 = {};
+  bf16x8 an[MT], bn[EPL];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) an[m] = xok[m] ? *(const bf16x8 *)(xrow[m]) : zero8;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) bn[j] = wok[j] ? *(const bf16x8 *)(wrow[j]) : zero8;
+  for (int kk = 0; kk < d; kk += 32) {
+    bf16x8 ac[MT], bc[EPL];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) ac[m] = an[m];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) bc[j] = bn[j];
+    if (kk + 32 < d) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) an[m] = xok[m] ? *(const bf16x8 *)(xrow[m] + kk + 32) : zero8;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) bn[j] = wok[j] ? *(const bf16x8 *)(wrow[j] + kk + 32) : zero8;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac[m], bc[j], acc[m][j], 0, 0, 0);
+  }
+  // logits -> LDS: lane holds expert column r16 of each block, rows 4*(lane>>4)+i
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = (wave + 4 * j) * 16 + r16;
+      if (e < E) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zl[(m * 16 + (lane >> 4) * 4 + i) * ldz + e] = acc[m][j][i];
+      }
+    }
+  __syncthreads();
+  for (int tl = wave; tl < BT; tl += 4) {
+    const int64_t t = t0 + tl;
+    if (t < a.T) select_token<EPL>(a, zl + tl * ldz, t, lane);
+  }
+}
+
+// fp32 layers: logits by FMA (small layers; correctness path).
+template <int EPL>
+__global__ __launch_bounds__(256) void route_learned_f32(const RouteArgs a) {
+  constexpr int BT = 16;
+  extern __shared__ float zl[];                 // [BT][E + 1]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
+  const int E = a.E, d = a.d, ldz = E + 1;
+  const float *x = (const float *)a.x;
+  const float *w = (const float *)a.w;
+  for (int p = threadIdx.x; p < BT * E; p += 256) {
+    const int tl = p / E, e = p - tl * E;
+    const int64_t t = t0 + tl;
+    float z = 0.f;
+    if (t < a.T) {
+      const float *xr = x + t * d;
+      const float *wr = w + (int64_t)e * d;
+      for (int kk = 0; kk < d; ++kk) z = fmaf(xr[kk], wr[kk], z);
+    }
+    zl[tl * ldz + e] = z;
+  }
+  __syncthreads();
+  for (int tl = wave; tl < BT; tl += 4) {
+    const int64_t t = t0 + tl;
+    if (t < a.T) select_token<EPL>(a, zl + tl * ldz, t, lane);
+  }
+}
+
+__global__ __launch_bounds__(256) void route_hash(const int32_t *token_ids, const int32_t *tid2eid,
+                                                  int64_t T, int k, int64_t vocab, float wval,
+                                                  float *weights, int32_t *indices,
+                                                  uint32_t *flags) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= T * k) return;
+  const int64_t t = p / k;
+  const int j = (int)(p - t * k);
+  const int64_t id = token_ids[t];
+  const bool ok = id >= 0 && id < vocab;
+  indices[p] = tid2eid[(ok ? id : 0) * k + j];
+  weights[p] = ok ? wval : 0.f;
+  if (!ok && flags) atomicOr(flags, (uint32_t)MOE_FLAG_TOKEN_ID_RANGE);
+}
+
+// ---------------------------------------------------------------------------
+template <int EPL>
+static hipError_t launch_learned_epl(const RouteArgs &a, int act_dtype, hipStream_t s) {
+  if (act_dtype == MOE_DTYPE_BF16) {
+    const int MT = a.T >= 2048 ? 2 : 1;
+    const int BT = 16 * MT;
+    const size_t lds = (size_t)BT * (a.E + 1) * sizeof(float);
+    const dim3 grid((unsigned)((a.T + BT - 1) / BT));
+    if (MT == 2)
+      hipLaunchKernelGGL((route_learned_bf16<EPL, 2>), grid, dim3(256), lds, s, a);
+    else
+      hipLaunchKernelGGL((route_learned_bf16<EPL, 1>), grid, dim3(256), lds, s, a);
+  } else {
+    const size_t lds = (size_t)16 * (a.E + 1) * sizeof(float);
+    const dim3 grid((unsigned)((a.T + 15) / 16));
+    hipLaunchKernelGGL((route_learned_f32<EPL>), grid, dim3(256), lds, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_learned(const moe_config &cfg, const void *x, const void *gate_w,
+                                const float *bias, int64_t T, float *weights,
+                                int32_t *indices, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  RouteArgs a;
+  a.x = x; a.w = gate_w; a.bias = bias; a.T = T;
+  a.d = cfg.dim; a.E = cfg.n_routed_experts; a.k = cfg.n_activated_experts;
+  a.G = cfg.n_expert_groups; a.topk_groups = cfg.n_limited_groups;
+  a.score_func = cfg.score_func;
+  a.renorm = cfg.renormalize < 0 ? (cfg.score_func != MOE_SCORE_SOFTMAX) : (cfg.renormalize != 0);
+  a.route_scale = cfg.route_scale;
+  a.weights = weights; a.indices = indices;
+  const int epl = (a.E + 63) / 64;
+  switch (epl) {
+    case 1: return launch_learned_epl<1>(a, cfg.act_dtype, s);
+    case 2: return launch_learned_epl<2>(a, cfg.act_dtype, s);
+    case 3: return launch_learned_epl<3>(a, cfg.act_dtype, s);
+    case 4: return launch_learned_epl<4>(a, cfg.act_dtype, s);
+    case 5: return launch_learned_epl<5>(a, cfg.act_dtype, s);
+    case 6: return launch_learned_epl<6>(a, cfg.act_dtype, s);
+    case 7: return launch_learned_epl<7>(a, cfg.act_dtype, s);
+    case 8: return launch_learned_epl<8>(a, cfg.act_dtype, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_route_hash(const moe_config &cfg, const int32_t *token_ids,
+                             const int32_t *tid2eid, int64_t T, float *weights,
+                             int32_t *indices, uint32_t *flags, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int k = cfg.n_activated_experts;
+  const int64_t n = T * k;
+  const float wval = cfg.route_scale / (float)k;
+  hipLaunchKernelGGL(route_hash, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, token_ids,
+                     tid2eid, T, k, cfg.vocab_size, wval, weights, indices, flags);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,127 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+binding, run the oracle on the same synthetic inputs, compare."""
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp4": 5e-2}     # max relative error of y
+WEIGHT_RTOL = 1e-5                                  # routing weights
+TIE_RTOL = 1e-6                                     # near-tie exemption
+
+
+def f64(t):
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def cpu_np(t):
+    return t.detach().cpu().numpy()
+
+
+def expert_fetcher(layer, cfg):
+    """expert(e) -> float64 (w_gate, w_up, w_down), decoded by the oracle for FP4."""
+    def get(e):
+        if cfg.expert_dtype == "fp4":
+            return (oracle.fp4_decode(cpu_np(layer["w_gate"][e]), cpu_np(layer["s_gate"][e])),
+                    oracle.fp4_decode(cpu_np(layer["w_up"][e]), cpu_np(layer["s_up"][e])),
+                    oracle.fp4_decode(cpu_np(layer["w_down"][e]), cpu_np(layer["s_down"][e])))
+        return f64(layer["w_gate"][e]), f64(layer["w_up"][e]), f64(layer["w_down"][e])
+    return get
+
+
+def shared_weights(layer, cfg):
+    if not cfg.n_shared_experts:
+        return None
+    return f64(layer["sh_gate"]), f64(layer["sh_up"]), f64(layer["sh_down"])
+
+
+def oracle_route(cfg, layer, tid2eid_oracle=None, rows=None):
+    """Oracle routing of all tokens (or of `rows`)."""
+    if cfg.route_mode == "hash":
+        ids = cpu_np(layer["token_ids"]).astype(np.int64)
+        if rows is not None:
+            ids = ids[rows]
+        w, idx = oracle.hash_gate(ids, tid2eid_oracle, cfg.route_scale)
+        return w, idx, None
+    x = f64(layer["x"]) if rows is None else f64(layer["x"][torch.as_tensor(rows)])
+    bias = None if layer["gate_bias"] is None else cpu_np(layer["gate_bias"])
+    return oracle.learned_gate(
+        x, f64(layer["gate_w"]), bias, score_func=cfg.score_func, n_groups=cfg.n_expert_groups,
+        topk_groups=cfg.n_limited_groups, topk=cfg.n_activated_experts,
+        route_scale=cfg.route_scale, renormalize=cfg.renormalize)
+
+
+def near_tie_tokens(cfg, aux):
+    """Tokens whose routing is not unique at the north-star's 1e-6 relative
+    tolerance: among the top k+1 fp32 keys (after the group mask) two
+    neighbours are that close, or the kept/dropped group scores are."""
+    if aux is None:
+        return np.zeros(0, dtype=bool)
+    keys = aux["masked_keys"].astype(np.float64)
+    T = keys.shape[0]
+    k = cfg.n_activated_experts
+    tie = np.zeros(T, dtype=bool)
+    for t in range(T):
+        row = np.sort(keys[t])[::-1][:k + 1]
+        row = row[np.isfinite(row)]
+        gaps = np.abs(np.diff(row))
+        scale = np.maximum(np.abs(row[:-1]), np.abs(row[1:]))
+        if np.any(gaps <= TIE_RTOL * scale):
+            tie[t] = True
+    if cfg.n_expert_groups > 1:
+        gs = np.sort(aux["group_scores"].astype(np.float64), axis=1)[:, ::-1]
+        g = cfg.n_limited_groups
+        if g < cfg.n_expert_groups:
+            a, b = gs[:, g - 1], gs[:, g]
+            tie |= np.abs(a - b) <= TIE_RTOL * np.maximum(np.abs(a), np.abs(b))
+    return tie
+
+
+def compare_routing(cfg, gpu_w, gpu_idx, ora_w, ora_idx, aux):
+    """Bit-exact indices except near-tie tokens; weights to WEIGHT_RTOL.
+    Returns the boolean mask of tokens whose routing differs (all exempt)."""
+    gpu_idx = np.asarray(gpu_idx, dtype=np.int64)
+    differ = np.any(gpu_idx != ora_idx, axis=1)
+    if differ.any():
+        tie = near_tie_tokens(cfg, aux)
+        bad = np.nonzero(differ & ~tie)[0]
+        assert bad.size == 0, (
+            f"{bad.size} tokens routed differently without a near tie, e.g. token {bad[0]}: "
+            f"gpu {gpu_idx[bad[0]]} oracle {ora_idx[bad[0]]}")
+        assert differ.sum() <= max(2, 0.01 * differ.size), f"too many near-tie tokens: {differ.sum()}"
+    same = ~differ
+    np.testing.assert_allclose(np.asarray(gpu_w, dtype=np.float64)[same], ora_w[same],
+                               rtol=WEIGHT_RTOL, atol=1e-7)
+    return differ
+
+
+def max_rel_err(y, ref):
+    denom = np.max(np.abs(ref))
+    return float(np.max(np.abs(y - ref)) / denom) if denom > 0 else float(np.max(np.abs(y)))
+
+
+def check_permutation_valid(indices, E, counts, offsets, sorted_tok, sorted_slot, inverse):
+    """Properties that pin a permutation by expert whatever the routing."""
+    indices = np.asarray(indices, dtype=np.int64)
+    T, k = indices.shape
+    np.testing.assert_array_equal(counts, np.bincount(indices.ravel(), minlength=E))
+    np.testing.assert_array_equal(offsets[:-1], np.concatenate([[0], np.cumsum(counts)[:-1]]))
+    assert offsets[-1] == T * k
+    sorted_tok = np.asarray(sorted_tok[:T * k], dtype=np.int64)
+    sorted_slot = np.asarray(sorted_slot[:T * k], dtype=np.int64)
+    # every row holds a pair of its segment's expert, tokens ascending (stable)
+    experts_of_rows = indices[sorted_tok, sorted_slot]
+    seg = np.repeat(np.arange(E), counts)
+    np.testing.assert_array_equal(experts_of_rows, seg)
+    key = sorted_tok * k + sorted_slot
+    for e in range(E):
+        s = key[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(s) > 0)
+    inverse = np.asarray(inverse, dtype=np.int64).reshape(T, k)
+    np.testing.assert_array_equal(sorted_tok[inverse.ravel()], np.repeat(np.arange(T), k))
+    np.testing.assert_array_equal(sorted_slot[inverse.ravel()], np.tile(np.arange(k), T))

@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: routing indices, counts and permutation bit-exact except tokens whose
+k-th / (k+1)-th keys (or kept / dropped group scores, or two selected keys)
+lie within 1e-6 relative; routing weights to 1e-5 relative; layer outputs
+max|y - y_ref| / max|y_ref| <= 2e-2 (bf16), 5e-2 (FP4), 1e-4 (fp32).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_ffn_route_amd import binding as B
+from mixture_experts_ffn_route_amd import config as C
+from mixture_experts_ffn_route_amd import synth
+from tests import parity_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+SMALL = list(C.SMALL_WORKLOADS)
+
+
+def _layer(workload, device):
+    layer = synth.make_layer(workload, device)
+    ora_table = None
+    if workload.cfg.route_mode == "hash":
+        cfg = workload.cfg
+        table, _, _, _ = B.moe_build_tid2eid(layer["p"], cfg.n_routed_experts,
+                                             cfg.n_activated_experts)
+        ora_table, _, _, _ = oracle.tid2eid_greedy(layer["p"], cfg.n_routed_experts,
+                                                   cfg.n_activated_experts)
+        assert np.array_equal(table, ora_table)
+        layer["tid2eid"] = torch.from_numpy(table).to(device)
+    return layer, ora_table
+
+
+def _forward(workload, layer, device):
+    cfg, T = workload.cfg, workload.T
+    ws = B.alloc_workspace(cfg, T, device)
+    y = torch.empty_like(layer["x"])
+    print(f"[forward] {workload.name} T={T}", flush=True)
+    B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y, ws)
+    torch.cuda.synchronize()
+    return y, ws
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_route_small(name, gpu):
+    wl = C.SMALL_WORKLOADS[name]
+    cfg, T = wl.cfg, wl.T
+    layer, ora_table = _layer(wl, gpu)
+    w = torch.empty((T, cfg.n_activated_experts), dtype=torch.float32, device=gpu)
+    idx = torch.empty((T, cfg.n_activated_experts), dtype=torch.int32, device=gpu)
+    print(f"[route] {name}", flush=True)
+    B.moe_route(cfg, layer, layer["x"], layer["token_ids"], T, w, idx)
+    torch.cuda.synchronize()
+    ow, oidx, aux = H.oracle_route(cfg, layer, ora_table)
+    differ = H.compare_routing(cfg, H.cpu_np(w), H.cpu_np(idx), ow, oidx, aux)
+    assert not differ.all()
+
+
+@pytest.mark.parametrize("E,k,T,seed", [(16, 2, 64, 0), (64, 4, 301, 1), (256, 8, 4096, 2),
+                                        (384, 8, 1000, 3), (1, 1, 17, 4), (1024, 3, 700, 5),
+                                        (7, 7, 5, 6)])
+def test_permute_random(E, k, T, seed, gpu):
+    rng = np.random.default_rng(seed)
+    indices = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    cfg = C.MoEConfig(dim=64, n_routed_experts=E, n_activated_experts=k, moe_inter_dim=64,
+                      route_mode="hash", vocab_size=1)
+    dev = lambda a: torch.from_numpy(a).to(gpu)
+    idx = dev(indices)
+    counts = torch.empty(E, dtype=torch.int32, device=gpu)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=gpu)
+    st = torch.empty(T * k, dtype=torch.int32, device=gpu)
+    ss = torch.empty(T * k, dtype=torch.int32, device=gpu)
+    inv = torch.empty(T * k, dtype=torch.int32, device=gpu)
+    flags = torch.zeros(4, dtype=torch.int32, device=gpu)
+    print(f"[permute] E={E} k={k} T={T}", flush=True)
+    B.moe_permute(cfg, idx, T, counts, offsets, st, ss, inv, flags)
+    torch.cuda.synchronize()
+    oc, oo, ost, oss, oinv = oracle.permute(indices, E)
+    np.testing.assert_array_equal(H.cpu_np(counts), oc)
+    np.testing.assert_array_equal(H.cpu_np(offsets), oo)
+    np.testing.assert_array_equal(H.cpu_np(st), ost)
+    np.testing.assert_array_equal(H.cpu_np(ss), oss)
+    np.testing.assert_array_equal(H.cpu_np(inv).reshape(T, k), oinv)
+    assert int(flags[0]) == 0
+
+
+def test_permute_drops_out_of_range_ids(gpu):
+    E, k, T = 8, 2, 50
+    rng = np.random.default_rng(7)
+    indices = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    indices[3, 1] = -1
+    indices[10, 0] = E
+    cfg = C.MoEConfig(dim=64, n_routed_experts=E, n_activated_experts=k, moe_inter_dim=64,
+                      route_mode="hash", vocab_size=1)
+    counts = torch.empty(E, dtype=torch.int32, device=gpu)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=gpu)
+    st = torch.empty(T * k, dtype=torch.int32, device=gpu)
+    ss = torch.empty(T * k, dtype=torch.int32, device=gpu)
+    inv = torch.empty(T * k, dtype=torch.int32, device=gpu)
+    flags = torch.zeros(4, dtype=torch.int32, device=gpu)
+    B.moe_permute(cfg, torch.from_numpy(indices).to(gpu), T, counts, offsets, st, ss, inv, flags)
+    torch.cuda.synchronize()
+    valid = (indices >= 0) & (indices < E)
+    oc, oo, ost, oss, oinv = oracle.permute(np.where(valid, indices, E), E + 1)
+    np.testing.assert_array_equal(H.cpu_np(counts), oc[:E])
+    assert int(offsets[E]) == valid.sum()
+    inv_np = H.cpu_np(inv).reshape(T, k)
+    assert inv_np[3, 1] == -1 and inv_np[10, 0] == -1
+    np.testing.assert_array_equal(inv_np[valid], oinv[valid])
+    assert int(flags[0]) & B.MOE_FLAG_EXPERT_RANGE
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_forward_small(name, gpu):
+    wl = C.SMALL_WORKLOADS[name]
+    cfg, T = wl.cfg, wl.T
+    layer, ora_table = _layer(wl, gpu)
+    y, ws = _forward(wl, layer, gpu)
+    v = B.workspace_views(cfg, T, ws)
+    ow, oidx, aux = H.oracle_route(cfg, layer, ora_table)
+    gidx = H.cpu_np(v["route_indices"])
+    differ = H.compare_routing(cfg, H.cpu_np(v["route_weights"]), gidx, ow, oidx, aux)
+    counts, offsets = H.cpu_np(v["counts"]), H.cpu_np(v["offsets"])
+    st, ss, inv = H.cpu_np(v["sorted_tok"]), H.cpu_np(v["sorted_slot"]), H.cpu_np(v["inverse"])
+    H.check_permutation_valid(gidx, cfg.n_routed_experts, counts, offsets, st, ss, inv)
+    if not differ.any():
+        oc, oo, ost, oss, oinv = oracle.permute(oidx, cfg.n_routed_experts)
+        np.testing.assert_array_equal(counts, oc)
+        np.testing.assert_array_equal(st[:T * cfg.n_activated_experts], ost)
+        np.testing.assert_array_equal(inv, oinv)
+    keep = ~differ
+    yref = oracle.layer_forward(H.f64(layer["x"])[keep], ow[keep], oidx[keep],
+                                H.expert_fetcher(layer, cfg), H.shared_weights(layer, cfg),
+                                cfg.swiglu_limit)
+    err = H.max_rel_err(H.f64(y)[keep], yref)
+    print(f"[forward] {name}: max rel err {err:.3e}", flush=True)
+    assert err <= H.TOL[cfg.expert_dtype if cfg.expert_dtype == "fp4" else cfg.act_dtype]
+    assert int(v["flags"][0]) == 0
+
+
+def test_forward_deterministic(gpu):
+    wl = C.SMALL_WORKLOADS["v3_small"]
+    layer, _ = _layer(wl, gpu)
+    y1, _ = _forward(wl, layer, gpu)
+    y2, _ = _forward(wl, layer, gpu)
+    assert torch.equal(y1, y2)
+
+
+def test_forward_t0_and_t1(gpu):
+    wl = C.SMALL_WORKLOADS["v3_small"]
+    cfg = wl.cfg
+    layer, _ = _layer(wl, gpu)
+    ws = B.alloc_workspace(cfg, 1, gpu)
+    y = torch.full((1, cfg.dim), 7.0, dtype=torch.bfloat16, device=gpu)
+    B.moe_forward(cfg, layer, layer["x"][:0], None, 0, y, ws)      # no-op
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    B.moe_forward(cfg, layer, layer["x"][:1], None, 1, y, ws)
+    torch.cuda.synchronize()
+    ow, oidx, _ = H.oracle_route(cfg, layer, rows=[0])
+    yref = oracle.layer_forward(H.f64(layer["x"][:1]), ow, oidx, H.expert_fetcher(layer, cfg),
+                                H.shared_weights(layer, cfg), cfg.swiglu_limit)
+    assert H.max_rel_err(H.f64(y), yref) <= H.TOL["bf16"]
+
+
+def test_forward_hash_skewed_multi_tile(gpu):
+    """Every token hits the same k experts: rows per expert = T spans several
+    GEMM tiles; the other experts get no rows."""
+    base = C.SMALL_WORKLOADS["hash_small"]
+    wl = C.Workload("hash_all_same", base.cfg, T=777)
+    cfg, T = wl.cfg, wl.T
+    layer = synth.make_layer(wl, gpu)
+    k = cfg.n_activated_experts
+    table = np.tile(np.array([3, 0, 9, 15][:k], dtype=np.int32), (cfg.vocab_size, 1))
+    layer["tid2eid"] = torch.from_numpy(table).to(gpu)
+    y, ws = _forward(wl, layer, gpu)
+    v = B.workspace_views(cfg, T, ws)
+    assert int(v["tile_count"][0]) > 2 * k
+    ow, oidx, _ = oracle.hash_gate(H.cpu_np(layer["token_ids"]), table, cfg.route_scale) + (None,)
+    yref = oracle.layer_forward(H.f64(layer["x"]), ow, oidx, H.expert_fetcher(layer, cfg),
+                                H.shared_weights(layer, cfg))
+    assert H.max_rel_err(H.f64(y), yref) <= H.TOL["bf16"]
+
+
+def test_forward_hash_bad_token_id_flagged(gpu):
+    wl = C.SMALL_WORKLOADS["hash_small"]
+    cfg, T = wl.cfg, wl.T
+    layer, _ = _layer(wl, gpu)
+    layer["token_ids"] = layer["token_ids"].clone()
+    layer["token_ids"][5] = cfg.vocab_size + 3
+    y, ws = _forward(wl, layer, gpu)
+    v = B.workspace_views(cfg, T, ws)
+    assert int(v["flags"][0]) & B.MOE_FLAG_TOKEN_ID_RANGE
+    assert torch.all(v["route_weights"][5] == 0)
