@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE FFN layer forward on one MI355X.
+
+A step is one full forward of the layer (route -> permute -> grouped GEMM1
+with SwiGLU -> grouped GEMM2 -> combine with the shared expert) over one
+batch of synthetic tokens, through the C ABI (moe_forward_profiled).  Inputs
+and weights are resident in HBM before the timed region starts.
+
+Prints one JSON line:
+  value        tokens/s of the DeepSeek-V3-shaped prefill layer (T=4096)
+  roofline     the dominant kernel (grouped GEMM1: gate|up + SwiGLU) against
+               its bound, timed with HIP events on the library's stream
+  cpu_baseline the float64 CPU oracle on a bounded sample of the same batch
+  decode       the T=64 decode layer of the same weights (tokens/s, GB/s)
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at V3 shape (T=4096 prefill, T=64 decode) + % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp4": 2500.0, "f32": 157.3}   # FP4 experts run on bf16 MFMA
+KERNEL_SOURCES = ("mixture_experts_ffn_route_amd/csrc/experts.hip",)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_counts(wl, counts):
+    """Method work per step counted from the actual routing (intermediates
+    such as H, Y and permuted copies are implementation traffic, excluded)."""
+    cfg, T = wl.cfg, wl.T
+    d, I, E, k = cfg.dim, cfg.moe_inter_dim, cfg.n_routed_experts, cfg.n_activated_experts
+    eb = 4 if cfg.act_dtype == "f32" else 2
+    if cfg.expert_dtype == "fp4":
+        mat = I * d * (0.5 + 1.0 / 32.0)          # codes + one scale byte per 32
+    else:
+        mat = I * d * eb
+    n_hit = int((counts > 0).sum())
+    sh = cfg.n_shared_experts
+    rows = T * k + T * sh
+    gemm1 = {"flops": 4.0 * d * I * rows,
+             "bytes": n_hit * 2 * mat + sh * 2 * I * d * eb + T * d * eb}
+    layer_flops = 6.0 * d * I * rows + (2.0 * T * d * E if cfg.route_mode == "learned" else 0.0)
+    layer_bytes = n_hit * 3 * mat + sh * 3 * I * d * eb + 2 * T * d * eb
+    layer_bytes += (E * d * eb + 4 * E) if cfg.route_mode == "learned" else 4 * T * k
+    return {"n_hit": n_hit, "gemm1": gemm1, "layer": {"flops": layer_flops, "bytes": layer_bytes}}
+
+
+def roofline_entry(flops, nbytes, seconds, peak_tflops):
+    t_mfma = flops / (peak_tflops * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        ach = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    ach = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_tflops, "unit": "TFLOP/s",
+            "frac": round(ach / peak_tflops, 4)}
+
+
+def load_traffic(workload_name, kernel="gemm1"):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm1_{workload_name}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def build_layer(wl, dev, B, synth):
+    layer = synth.make_layer(wl, dev)
+    if wl.cfg.route_mode == "hash":
+        import torch
+        table, _, _, _ = B.moe_build_tid2eid(layer["p"], wl.cfg.n_routed_experts,
+                                             wl.cfg.n_activated_experts)
+        layer["tid2eid"] = torch.from_numpy(table).to(dev)
+    return layer
+
+
+def time_workload(wl, layer, steps, warmup, B, torch):
+    cfg, T = wl.cfg, wl.T
+    dev = layer["x"].device
+    ws = B.alloc_workspace(cfg, T, dev)
+    y = torch.empty_like(layer["x"])
+    nst = len(B.MOE_STAGES)
+    ev = B.HipEvents((nst + 1) * steps)
+    for _ in range(warmup):
+        B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y, ws)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(steps):
+        B.moe_forward_profiled(cfg, layer, layer["x"], layer["token_ids"], T, y, ws,
+                               ev.handles[s * (nst + 1):(s + 1) * (nst + 1)])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    stage_ms = {name: 0.0 for name in B.MOE_STAGES}
+    for s in range(steps):
+        base = s * (nst + 1)
+        for i, name in enumerate(B.MOE_STAGES):
+            stage_ms[name] += ev.elapsed_ms(base + i, base + i + 1) / steps
+    ev.close()
+    views = B.workspace_views(cfg, T, ws)
+    counts = views["counts"].cpu().numpy()
+    return total_ms / steps, stage_ms, counts
+
+
+def workload_report(wl, ms, stage_ms, counts, peak):
+    alg = algorithmic_counts(wl, counts)
+    g1 = alg["gemm1"]
+    roof = roofline_entry(g1["flops"], g1["bytes"], stage_ms["gemm1"] / 1e3, peak)
+    lay = alg["layer"]
+    layer_roof = roofline_entry(lay["flops"], lay["bytes"], ms / 1e3, peak)
+    return {
+        "tokens_per_s": round(wl.T / (ms / 1e3), 1),
+        "ms_per_step": round(ms, 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "experts_hit": alg["n_hit"],
+        "gemm1": {**roof, "flops": g1["flops"], "bytes": g1["bytes"], "ms": round(stage_ms["gemm1"], 4)},
+        "layer": {**layer_roof, "flops": lay["flops"], "bytes": lay["bytes"]},
+    }
+
+
+def cpu_baseline(wl, layer, sample_tokens):
+    """The float64 oracle, as it is, on the first `sample_tokens` tokens:
+    routing + permutation + routed/shared SwiGLU forward."""
+    import numpy as np
+    import torch
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    cfg = wl.cfg
+    S = min(sample_tokens, wl.T)
+    f32 = lambda t: t.detach().float().cpu().numpy()
+    x = f32(layer["x"][:S])
+    table = None
+    if cfg.route_mode == "hash":
+        table, _, _, _ = oracle.tid2eid_greedy(layer["p"], cfg.n_routed_experts,
+                                               cfg.n_activated_experts)
+        ids = layer["token_ids"][:S].cpu().numpy()
+        _, idx = oracle.hash_gate(ids, table, cfg.route_scale)
+    else:
+        bias = None if layer["gate_bias"] is None else layer["gate_bias"].cpu().numpy()
+        gate_w = f32(layer["gate_w"])
+        _, idx, _ = oracle.learned_gate(x, gate_w, bias, score_func=cfg.score_func,
+                                        n_groups=cfg.n_expert_groups,
+                                        topk_groups=cfg.n_limited_groups,
+                                        topk=cfg.n_activated_experts, route_scale=cfg.route_scale)
+    # host copies of the experts the sample touches (data staging, untimed)
+    host = {}
+    for e in np.unique(idx):
+        e = int(e)
+        if cfg.expert_dtype == "fp4":
+            host[e] = tuple((layer[n][e].cpu().numpy(), layer["s_" + n[2:]][e].cpu().numpy())
+                            for n in ("w_gate", "w_up", "w_down"))
+        else:
+            host[e] = tuple(f32(layer[n][e]) for n in ("w_gate", "w_up", "w_down"))
+    shared = None
+    if cfg.n_shared_experts:
+        shared_host = tuple(f32(layer[n]) for n in ("sh_gate", "sh_up", "sh_down"))
+
+    def expert(e):
+        if cfg.expert_dtype == "fp4":
+            return tuple(oracle.fp4_decode(p, s) for p, s in host[e])
+        return tuple(a.astype(np.float64) for a in host[e])
+
+    t0 = time.perf_counter()
+    if cfg.route_mode == "hash":
+        w, idx = oracle.hash_gate(layer["token_ids"][:S].cpu().numpy(), table, cfg.route_scale)
+    else:
+        w, idx, _ = oracle.learned_gate(x, gate_w, bias, score_func=cfg.score_func,
+                                        n_groups=cfg.n_expert_groups,
+                                        topk_groups=cfg.n_limited_groups,
+                                        topk=cfg.n_activated_experts, route_scale=cfg.route_scale)
+    oracle.permute(idx, cfg.n_routed_experts)
+    if cfg.n_shared_experts:
+        shared = tuple(a.astype(np.float64) for a in shared_host)
+    oracle.layer_forward(x, w, idx, expert, shared, cfg.swiglu_limit)
+    dt = time.perf_counter() - t0
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {"value": round(S / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of the {wl.T} tokens of {wl.name}: route + permute + routed and "
+                      f"shared SwiGLU in float64 ({len(host)} experts touched), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_prefill")
+    ap.add_argument("--decode", default="v3_decode", help="second workload ('' to skip)")
+    ap.add_argument("--extra", default="", help="comma-separated extra workloads to report")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: every box here has one MI355X and this layer "
+              f"holds all experts on one GPU (asked for --gpus {args.gpus}, WORLD_SIZE={world})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_ffn_route_amd import binding as B
+    from mixture_experts_ffn_route_amd import config as C
+    from mixture_experts_ffn_route_amd import synth
+
+    dev = torch.device("cuda:0")
+    wl = C.FULL_WORKLOADS[args.workload]
+    log(f"generating {wl.name} inputs on {torch.cuda.get_device_name(0)}")
+    t = time.time()
+    layer = build_layer(wl, dev, B, synth)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t:.1f} s; timing {args.steps} steps after {args.warmup} warmup")
+    peak = MFMA_PEAK_TFLOPS[wl.cfg.expert_dtype if wl.cfg.expert_dtype == "fp4" else wl.cfg.act_dtype]
+    ms, stage_ms, counts = time_workload(wl, layer, args.steps, args.warmup, B, torch)
+    rep = workload_report(wl, ms, stage_ms, counts, peak)
+    log(f"{wl.name}: {rep['ms_per_step']} ms/step, {rep['tokens_per_s']} tokens/s, stages {rep['stage_ms']}")
+
+    out = {
+        "metric": METRIC,
+        "value": rep["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rep["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4" if wl.cfg.expert_dtype == "fp4" else wl.cfg.act_dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "dim": wl.cfg.dim,
+                   "n_routed_experts": wl.cfg.n_routed_experts,
+                   "n_activated_experts": wl.cfg.n_activated_experts,
+                   "moe_inter_dim": wl.cfg.moe_inter_dim,
+                   "n_shared_experts": wl.cfg.n_shared_experts,
+                   "parallelism": "single-gpu (all experts resident)"},
+    }
+    g1 = rep["gemm1"]
+    out["roofline"] = {"kernel": "grouped_gemm1 (gate|up + SwiGLU)", "bound": g1["bound"],
+                       "achieved": g1["achieved"], "peak": g1["peak"], "unit": g1["unit"],
+                       "frac": g1["frac"], "traffic": load_traffic(wl.name),
+                       "algorithmic_bytes": g1["bytes"], "algorithmic_flops": g1["flops"],
+                       "avg_ms": g1["ms"]}
+    out["layer_roofline"] = rep["layer"]
+    out["stage_ms"] = rep["stage_ms"]
+
+    reports = {}
+    names = ([args.decode] if args.decode else []) + [n for n in args.extra.split(",") if n]
+    for name in names:
+        w2 = C.FULL_WORKLOADS[name]
+        if w2.cfg == wl.cfg and w2.seed == wl.seed and max(w2.T, w2.x_rows) == wl.T:
+            # same layer and weights; x is the first T rows of the same draw
+            l2 = dict(layer)
+            l2["x"] = layer["x"][:w2.T].contiguous()
+        else:
+            log(f"generating {name} inputs")
+            l2 = build_layer(w2, dev, B, synth)
+        p2 = MFMA_PEAK_TFLOPS[w2.cfg.expert_dtype if w2.cfg.expert_dtype == "fp4" else w2.cfg.act_dtype]
+        ms2, st2, c2 = time_workload(w2, l2, args.steps, args.warmup, B, torch)
+        r2 = workload_report(w2, ms2, st2, c2, p2)
+        r2["roofline"] = {k: r2["gemm1"][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+        r2["roofline"]["traffic"] = load_traffic(name)
+        reports[name] = r2
+        log(f"{name}: {r2['ms_per_step']} ms/step, {r2['tokens_per_s']} tokens/s, stages {r2['stage_ms']}")
+        if l2 is not layer:
+            del l2
+    if args.decode:
+        out["decode"] = {"workload": args.decode, **reports.pop(args.decode)}
+    if reports:
+        out["extra_workloads"] = reports
+
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_sample_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(wl, layer, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -211,6 +211,24 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                 const int32_t *token_ids, int64_t T, void *y,
                 void *ws, size_t ws_bytes, void *stream);
 
+/* Stages of moe_forward in launch order (for moe_forward_profiled). */
+#define MOE_STAGE_ROUTE 0     /* router kernel (or hash gather)                  */
+#define MOE_STAGE_PERMUTE 1   /* permute kernel                                 */
+#define MOE_STAGE_GEMM1 2     /* gate|up grouped GEMM + SwiGLU (routed + shared) */
+#define MOE_STAGE_GEMM2 3     /* down grouped GEMM x gate value                  */
+#define MOE_STAGE_COMBINE 4   /* gather-combine into y                          */
+#define MOE_STAGE_COUNT 5
+
+/* moe_forward that also records a timing event on `stream` before each stage
+ * and after the last one, so the caller can time every kernel of the call.
+ *   events (host) [MOE_STAGE_COUNT + 1] hipEvent_t handles created by the
+ *   caller (hipEventCreate); event i precedes stage i, event COUNT follows
+ *   the combine.  Results are identical to moe_forward's.  A failed
+ *   hipEventRecord returns MOE_ERR_HIP. */
+int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void *x,
+                         const int32_t *token_ids, int64_t T, void *y,
+                         void *ws, size_t ws_bytes, void **events, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,8 +26,9 @@ MOE_FLAG_EXPERT_RANGE = 2
 
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout",
-    "moe_workspace_size", "moe_route", "moe_permute", "moe_forward",
+    "moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_profiled",
 )
+MOE_STAGES = ("route", "permute", "gemm1", "gemm2", "combine")
 
 
 class MoeConfigC(ctypes.Structure):
@@ -72,8 +73,10 @@ def _load():
     lib.moe_route.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, vp]
     lib.moe_permute.argtypes = [cfgp, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_forward.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_forward_profiled.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t,
+                                         ctypes.POINTER(ctypes.c_void_p), vp]
     for f in ("moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout", "moe_route",
-              "moe_permute", "moe_forward"):
+              "moe_permute", "moe_forward", "moe_forward_profiled"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -175,6 +178,43 @@ def moe_forward(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, ws, stream
     _check(_lib.moe_forward(ctypes.byref(config_c(cfg)), ctypes.byref(weights_c(layer)), _ptr(x),
                             _ptr(token_ids), T, _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_profiled(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, ws, events,
+                         stream=None):
+    """events: len(MOE_STAGES) + 1 raw hipEvent_t handles (see HipEvents)."""
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(_lib.moe_forward_profiled(ctypes.byref(config_c(cfg)), ctypes.byref(weights_c(layer)),
+                                     _ptr(x), _ptr(token_ids), T, _ptr(y), _ptr(ws),
+                                     ws.numel() * ws.element_size(), arr, _stream(stream)),
+           "moe_forward_profiled")
+
+
+class HipEvents:
+    """Raw HIP timing events from the HIP runtime torch already loaded."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.handles[a]),
+                                        ctypes.c_void_p(self.handles[b])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self.hip.hipEventDestroy(ctypes.c_void_p(h))
+        self.handles = []
 
 
 # ---------------------------------------------------------------------------

@@ -418,11 +418,16 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
   return run_gemm_mb<1, 1, false, 3>(mb, a, max_tiles, s);
 }
 
+static hipError_t mark(const ExpertPlan &p, int i, hipStream_t s) {
+  return p.events ? hipEventRecord(p.events[i], s) : hipSuccess;
+}
+
 hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   const int64_t routed_rows = p.T * p.k;
   const int64_t total_rows = routed_rows + (p.has_shared ? p.T : 0);
   const moe_weights &w = *p.w;
   hipError_t err;
+  if ((err = mark(p, MOE_STAGE_GEMM1, s)) != hipSuccess) return err;
   if (p.act_dtype == MOE_DTYPE_F32) {
     const dim3 g1((unsigned)((p.inter + 255) / 256), (unsigned)total_rows);
     hipLaunchKernelGGL(expert_up_f32, g1, dim3(256), 0, s, (const float *)p.x, p.sorted_tok,
@@ -431,16 +436,19 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
                        (const float *)w.sh_gate, (const float *)w.sh_up, p.swiglu_limit,
                        (float *)p.h);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = mark(p, MOE_STAGE_GEMM2, s)) != hipSuccess) return err;
     const dim3 g2((unsigned)((p.dim + 255) / 256), (unsigned)total_rows);
     hipLaunchKernelGGL(expert_down_f32, g2, dim3(256), 0, s, (const float *)p.h, p.sorted_tok,
                        p.sorted_slot, p.route_idx, p.route_w, p.offsets, p.E, p.k, routed_rows,
                        total_rows, p.dim, p.inter, (const float *)w.w_down,
                        (const float *)w.sh_down, (float *)p.yrows);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = mark(p, MOE_STAGE_COMBINE, s)) != hipSuccess) return err;
     hipLaunchKernelGGL(combine_f32, dim3((unsigned)p.T), dim3(256), 0, s,
                        (const float *)p.yrows, p.inverse, p.k, p.dim,
                        p.has_shared ? routed_rows : (int64_t)-1, (float *)p.y);
-    return hipGetLastError();
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return mark(p, MOE_STAGE_COUNT, s);
   }
 
   const int mb = p.tile_rows / 16;
@@ -480,6 +488,7 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   }
 
   // GEMM2: down * gate value -> Y rows
+  if ((err = mark(p, MOE_STAGE_GEMM2, s)) != hipSuccess) return err;
   a.A = (const bf16 *)p.h;
   a.a_rows = nullptr;
   a.K = p.inter;
@@ -502,10 +511,12 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
     if ((err = gemm_launch(1, false, mb, a, p.max_tiles, s)) != hipSuccess) return err;
   }
 
+  if ((err = mark(p, MOE_STAGE_COMBINE, s)) != hipSuccess) return err;
   hipLaunchKernelGGL(combine_bf16, dim3((unsigned)p.T), dim3(256), 0, s, (const bf16 *)p.yrows,
                      p.inverse, p.k, p.dim, p.has_shared ? routed_rows : (int64_t)-1,
                      (bf16 *)p.y);
-  return hipGetLastError();
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  return mark(p, MOE_STAGE_COUNT, s);
 }
 
 }  // namespace moe

@@ -49,6 +49,7 @@ struct ExpertPlan {
   const int32_t *tiles, *tile_count;
   int max_tiles, tile_rows, n_shared_tiles;
   void *h, *yrows, *y;
+  hipEvent_t *events;    // null, or [MOE_STAGE_COUNT + 1] stage timing events
 };
 
 // Rows per GEMM tile chosen for a layer of T tokens (depends on the

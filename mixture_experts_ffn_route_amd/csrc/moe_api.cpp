@@ -205,9 +205,9 @@ int moe_permute(const moe_config *cfg, const int32_t *indices, int64_t T, int32_
                                         inverse, flags, nullptr, false, (hipStream_t)stream));
 }
 
-int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
-                const int32_t *token_ids, int64_t T, void *y, void *ws, size_t ws_bytes,
-                void *stream) {
+static int forward_impl(const moe_config *cfg, const moe_weights *w, const void *x,
+                        const int32_t *token_ids, int64_t T, void *y, void *ws, size_t ws_bytes,
+                        hipEvent_t *events, void *stream) {
   moe_ws_layout L;
   int st = make_layout(cfg, T, &L);
   if (st != MOE_OK) return st;
@@ -242,6 +242,7 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
   const bool hash = cfg->route_mode == MOE_ROUTE_HASH;
 
   hipError_t e;
+  if (events && hipEventRecord(events[MOE_STAGE_ROUTE], s) != hipSuccess) return MOE_ERR_HIP;
   if (hash) {
     if ((e = moe::launch_clear_flags(flags, s)) != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, route_w, route_idx, flags, s);
@@ -256,6 +257,7 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
   ts.tile_rows = L.tile_rows;
   ts.n_shared_tiles = cfg->n_shared_experts ? (int)((T + L.tile_rows - 1) / L.tile_rows) : 0;
   ts.shared_rows_tok = sorted_tok + T * k;
+  if (events && hipEventRecord(events[MOE_STAGE_PERMUTE], s) != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_permute(cfg->n_routed_experts, k, T, route_idx, counts, offsets, sorted_tok,
                           sorted_slot, inverse, flags, &ts, /*clear_flags=*/!hash, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -286,7 +288,23 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
   p.h = base + L.h;
   p.yrows = base + L.yrows;
   p.y = y;
+  p.events = events;
   return hip_status(moe::launch_experts(p, s));
+}
+
+int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
+                const int32_t *token_ids, int64_t T, void *y, void *ws, size_t ws_bytes,
+                void *stream) {
+  return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, nullptr, stream);
+}
+
+int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void *x,
+                         const int32_t *token_ids, int64_t T, void *y, void *ws,
+                         size_t ws_bytes, void **events, void *stream) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, (hipEvent_t *)events, stream);
 }
 
 }  // extern "C"
