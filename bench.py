@@ -217,7 +217,20 @@ def main():
     ap.add_argument("--extra", default="", help="comma-separated extra workloads to report")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

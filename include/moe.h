@@ -121,6 +121,7 @@ typedef struct {
   size_t sorted_tok;           /* int32 [T*k + T] token of each permuted row;
                                   rows T*k.. are the shared expert's (row-T*k)   */
   size_t sorted_slot;          /* int32 [T*k]    slot of each permuted row       */
+  size_t sorted_weight;        /* float [T*k]    gate value of each permuted row */
   size_t inverse;              /* int32 [T, k]   permuted row of pair (t, j)     */
   size_t tiles;                /* int32 [max_tiles, 4] GEMM work list           */
   size_t tile_count;           /* int32 [1]      tiles written by the permute    */

@@ -53,7 +53,7 @@ class MoeWeightsC(ctypes.Structure):
 class MoeWsLayoutC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total_bytes", "route_weights", "route_indices", "counts", "offsets", "sorted_tok",
-        "sorted_slot", "inverse", "tiles", "tile_count", "flags", "h", "yrows")] + [
+        "sorted_slot", "sorted_weight", "inverse", "tiles", "tile_count", "flags", "h", "yrows")] + [
         ("max_tiles", ctypes.c_int32), ("tile_rows", ctypes.c_int32)]
 
 
@@ -246,6 +246,7 @@ def workspace_views(cfg: MoEConfig, T: int, ws):
         "offsets": view(lay["offsets"], E + 1, torch.int32),
         "sorted_tok": view(lay["sorted_tok"], T * k + T, torch.int32),
         "sorted_slot": view(lay["sorted_slot"], T * k, torch.int32),
+        "sorted_weight": view(lay["sorted_weight"], T * k, torch.float32),
         "inverse": view(lay["inverse"], T * k, torch.int32).view(T, k),
         "tiles": view(lay["tiles"], 4 * lay["max_tiles"], torch.int32).view(-1, 4),
         "tile_count": view(lay["tile_count"], 1, torch.int32),

@@ -44,63 +44,104 @@ struct GemmArgs {
   int tile_begin, tile_end;  // tile_end < 0: end = *tile_count
   int n_slabs;
   float limit;               // SwiGLU clamp (two-matrix form); <= 0: none
-  const float *route_w;      // one-matrix form: gate value of each (token, slot)
-  const int32_t *sorted_tok, *sorted_slot;
-  int k;
+  const float *sorted_w;     // one-matrix form: gate value of each permuted row
   int64_t routed_rows;       // T * k: rows at or above this belong to the shared expert
 };
 
-template <int NB, int NCB, int MB, bool FP4, int PF>
-__global__ __launch_bounds__(256) void grouped_gemm(const GemmArgs g) {
-  constexpr int WAVES = 4;
-  constexpr int BK = FP4 ? 128 : 64;       // K per LDS stage
+#define MOE_LDS __attribute__((address_space(3)))
+#define MOE_GLOBAL __attribute__((address_space(1)))
+
+// 16-byte asynchronous global -> LDS copy: lane l's 16 bytes land at
+// lds_block + 16*l (lds_block must be wave-uniform).  Completion is tracked by
+// vmcnt like any vector load.
+__device__ __forceinline__ void dma16(const void *gsrc, void *lds_block) {
+  __builtin_amdgcn_global_load_lds((MOE_GLOBAL void *)gsrc, (MOE_LDS void *)lds_block, 16, 0, 0);
+}
+
+// s_waitcnt immediate for vmcnt(n) (gfx9 encoding: vmcnt[3:0] in bits 3:0,
+// vmcnt[5:4] in bits 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima,
+// i.e. not waited on).
+#define MOE_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Row blocks are processed in chunks of MCH (a tile's block count is rounded
+// up to a multiple of MCH): every pipeline stage is then straight-line code
+// in which the LDS reads of a chunk issue back to back and the MFMAs of one
+// chunk overlap the reads of the next.  Padding blocks read real rows (the
+// tile's last row) and are never stored.
+constexpr int MCH = 4;
+
+struct TileCtx {
+  int grp, row0, rows, col0, lane, wave, K, N;
+  bool shared;
+};
+
+// One tile: MBE row blocks (compile time), NB weight matrices (2: gate|up
+// with the SwiGLU epilogue, 1: down with the gate-value epilogue), NCB
+// 16-column blocks per wave and matrix, FP4 or bf16 weights, NS-deep load
+// pipeline.  SLOT = bf16 elements per LDS ring slot.
+//
+// Stage = BK inputs.  Per stage each wave issues (a) its share of the tile's
+// A fragments as asynchronous global->LDS copies -- fragment (row block m,
+// k-step s) is 64 lanes x 16 bytes, row 16m + (lane & 15) of the gathered
+// activations, so the LDS block already has the MFMA A-operand layout and the
+// readers take 16 consecutive bytes per lane without bank conflicts -- and
+// (b) its own weight columns as 16-byte loads into a register ring.  Stage st
+// is consumed NS-1 stages after it was issued; one vmcnt wait and one barrier
+// per stage.
+template <int WAVES, int NB, int NCB, int MBE, bool FP4, int NS, int SLOT>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, bf16 *As) {
+  constexpr int BK = FP4 ? 128 : 64;       // inputs per stage
   constexpr int SUBS = BK / 32;            // MFMA k-steps per stage
-  constexpr int CPR = BK / 8;              // 16-byte chunks per A row per stage
-  constexpr int BM = MB * 16;
-  constexpr int ACH = BM * CPR;
-  constexpr int ACH_T = (ACH + 255) / 256;
-  constexpr int NQ = FP4 ? 1 : SUBS;       // 16-byte B loads per (matrix, block) per stage
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM * BK];
+  constexpr int FRAG = 512;                // bf16 per 16x32 A fragment (1 KB)
+  constexpr int NFRAG = MBE * SUBS;        // A fragments per stage
+  constexpr int NFW = (NFRAG + WAVES - 1) / WAVES;
+  constexpr int NQ = FP4 ? 1 : SUBS;       // 16-byte weight loads per (matrix, block) per stage
+  constexpr int NBV = NB * NCB * (FP4 ? 2 : NQ);   // weight-side vector memory ops per stage
+  constexpr int VM_PER_STAGE = NFW + NBV;          // every wave issues exactly this many
+  constexpr int CH = MBE < MCH ? MBE : MCH;
+  static_assert(NS >= 2, "pipeline needs two stages");
+  static_assert((NS - 2) * VM_PER_STAGE <= 63, "vmcnt holds 6 bits");
+  static_assert(NFW * WAVES * FRAG <= SLOT, "ring slot too small");
+  static_assert(MBE % CH == 0, "row blocks come in whole chunks");
 
-  // ---- work item (XCD-aware) ----
-  const int tend = g.tile_end >= 0 ? g.tile_end : *g.tile_count;
-  const int64_t work = (int64_t)(tend - g.tile_begin) * g.n_slabs;
-  const int xcd = blockIdx.x & 7;
-  const int64_t slot = blockIdx.x >> 3;
-  const int64_t per_xcd = (work + 7) >> 3;
-  if (slot >= per_xcd) return;
-  const int64_t item = xcd * per_xcd + slot;
-  if (item >= work) return;
-  const int tile = g.tile_begin + (int)(item / g.n_slabs);
-  const int slab = (int)(item - (int64_t)(tile - g.tile_begin) * g.n_slabs);
-  const int grp = g.tiles[4 * tile], row0 = g.tiles[4 * tile + 1], rows = g.tiles[4 * tile + 2];
-  const int nmb = (rows + 15) >> 4;
-  const bool shared = grp == g.E;
-  const int K = g.K, N = g.N;
+  const int lane = t.lane, wave = t.wave, r16 = lane & 15, jq = lane >> 4;
+  const int K = t.K, N = t.N, rows = t.rows, row0 = t.row0, col0 = t.col0;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, jq = lane >> 4;
-  const int col0 = slab * (WAVES * NCB * 16) + wave * NCB * 16;
-
-  // ---- A staging assignment: chunk c -> (row, 16-byte chunk) ----
-  const bf16 *asrc[ACH_T];
-  int adst[ACH_T];
+  // down GEMM: gate value of each output row this lane stores (rows
+  // 16m + 4jq + i), loaded up front so the latency hides under the main loop.
+  // (The LDS holds nothing but the copy ring: with a second LDS object the
+  // compiler adds a full vmcnt drain before every LDS read.)
+  float row_w[NB == 1 ? MBE : 1][4];
+  if constexpr (NB == 1) {
 #pragma unroll
-  for (int i = 0; i < ACH_T; ++i) {
-    const int c = tid + 256 * i;
-    asrc[i] = nullptr;
-    adst[i] = -1;
-    if (c < nmb * 16 * CPR) {
-      const int r = c / CPR, ch = c - r * CPR;
-      adst[i] = r * BK + ((ch ^ (r & 7)) * 8);
-      if (r < rows) {
-        const int64_t src = g.a_rows ? g.a_rows[row0 + r] : (int64_t)(row0 + r);
-        asrc[i] = g.A + src * K + ch * 8;
+    for (int m = 0; m < MBE; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int r = m * 16 + jq * 4 + i;
+        r = r < rows ? r : rows - 1;
+        const int64_t R = row0 + r;
+        row_w[m][i] = R < g.routed_rows ? g.sorted_w[R < g.routed_rows ? R : 0] : 1.f;
       }
-    }
   }
 
-  // ---- B pointers ----
+  // ---- this wave's A fragments f = wave + WAVES*i (copies past NFRAG
+  // re-read fragment 0 into slots nobody reads, so every wave issues NFW) ----
+  const bf16 *asrc[NFW];
+#pragma unroll
+  for (int i = 0; i < NFW; ++i) {
+    const int f0 = wave + WAVES * i;
+    const int f = f0 < NFRAG ? f0 : 0;
+    const int m = f / SUBS, s = f - m * SUBS;
+    int r = m * 16 + r16;
+    r = r < rows ? r : rows - 1;
+    const int64_t src = g.a_rows ? g.a_rows[row0 + r] : (int64_t)(row0 + r);
+    // bf16 keeps k = 32s + 8jq; FP4 uses k = 32jq + 8s so that each lane's 32
+    // weight codes share one scale.  A and B use the same order.
+    const int koff = FP4 ? (32 * jq + 8 * s) : (32 * s + 8 * jq);
+    asrc[i] = g.A + src * K + koff;
+  }
+
+  // ---- weight pointers ----
   const uint8_t *bptr[NB][NCB];
   const uint8_t *sptr[NB][NCB];
 #pragma unroll
@@ -110,71 +151,66 @@ __global__ __launch_bounds__(256) void grouped_gemm(const GemmArgs g) {
       const int64_t n = col0 + cb * 16 + r16;
       if constexpr (FP4) {
         const int64_t K2 = K / 2, K32 = K / 32;
-        bptr[b][cb] = (const uint8_t *)g.B[b] + ((int64_t)grp * N + n) * K2 + jq * 16;
-        sptr[b][cb] = g.S[b] + ((int64_t)grp * N + n) * K32 + jq;
+        bptr[b][cb] = (const uint8_t *)g.B[b] + ((int64_t)t.grp * N + n) * K2 + jq * 16;
+        sptr[b][cb] = g.S[b] + ((int64_t)t.grp * N + n) * K32 + jq;
       } else {
-        const bf16 *base = shared ? g.SB[b] : (const bf16 *)g.B[b] + (int64_t)grp * N * K;
+        const bf16 *base = t.shared ? g.SB[b] : (const bf16 *)g.B[b] + (int64_t)t.grp * N * K;
         bptr[b][cb] = (const uint8_t *)(base + n * K + jq * 8);
         sptr[b][cb] = nullptr;
       }
     }
 
-  f32x4 acc[MB][NB][NCB];
+  f32x4 acc[MBE][NB][NCB];
 #pragma unroll
-  for (int m = 0; m < MB; ++m)
+  for (int m = 0; m < MBE; ++m)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[m][b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 bq[PF][NB][NCB][NQ];
-  uint32_t sq[PF][NB][NCB];
-  u32x4 areg[ACH_T];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  u32x4 bq[NS][NB][NCB][NQ];
+  uint32_t sq[NS][NB][NCB];
   const int nst = K / BK;
 
-  auto load_a = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < ACH_T; ++i)
-      areg[i] = asrc[i] ? *(const u32x4 *)(asrc[i] + (int64_t)st * BK) : zero4;
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH_T; ++i)
-      if (adst[i] >= 0) *(u32x4 *)(&As[buf][adst[i]]) = areg[i];
-  };
-
-#define MOE_LOAD_B(SLOT, ST)                                                          \
-  {                                                                                   \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                    \
-    _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) {                              \
-      if constexpr (FP4) {                                                            \
-        bq[SLOT][b][cb][0] = *(const u32x4 *)(bptr[b][cb] + (int64_t)(ST) * (BK / 2)); \
-        sq[SLOT][b][cb] = sptr[b][cb][(ST) * (BK / 32)];                              \
-      } else {                                                                        \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                \
-          bq[SLOT][b][cb][q] =                                                        \
-              *(const u32x4 *)(bptr[b][cb] + ((int64_t)(ST) * BK + q * 32) * 2);      \
-      }                                                                               \
-    }                                                                                 \
+#define MOE_ISSUE(SLOTI, ST)                                                              \
+  {                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < NFW; ++i)                                       \
+      dma16(asrc[i] + (int64_t)(ST) * BK, As + (SLOTI) * SLOT + (wave + WAVES * i) * FRAG); \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                        \
+    _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) {                                  \
+      if constexpr (FP4) {                                                                \
+        bq[SLOTI][b][cb][0] = *(const u32x4 *)(bptr[b][cb] + (int64_t)(ST) * (BK / 2));   \
+        sq[SLOTI][b][cb] = sptr[b][cb][(ST) * (BK / 32)];                                 \
+      } else {                                                                            \
+        _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                    \
+          bq[SLOTI][b][cb][q] =                                                           \
+              *(const u32x4 *)(bptr[b][cb] + ((int64_t)(ST) * BK + q * 32) * 2);          \
+      }                                                                                   \
+    }                                                                                     \
   }
 
-  // prologue
-  load_a(0);
-  store_a(0);
+  // prologue: stages 0 .. NS-2 (stage indices past the end re-read the
+  // last stage: same addresses, so they hit in L2 and cost no HBM bytes)
+  const int last = nst - 1;
 #pragma unroll
-  for (int p = 0; p < PF - 1; ++p)
-    if (p < nst) MOE_LOAD_B(p, p);
-  __syncthreads();
+  for (int p = 0; p < NS - 1; ++p) MOE_ISSUE(p, p < last ? p : last);
 
-  for (int s0 = 0; s0 < nst; s0 += PF) {
+  // Every iteration issues exactly one stage of loads per step, so the number
+  // of vector memory ops between a stage's issue and its use is the constant
+  // (NS-1) * VM_PER_STAGE and every wait below is a compile-time vmcnt.
+  for (int s0 = 0; s0 < nst; s0 += NS) {
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
+    for (int p = 0; p < NS; ++p) {
       const int st = s0 + p;
+      // stages st+1 .. st+NS-2 may stay in flight
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT((NS - 2) * VM_PER_STAGE));
+      __builtin_amdgcn_s_barrier();     // every wave's copies for st landed; st-1 fully read
+      {
+        const int nx = st + NS - 1;
+        MOE_ISSUE((p + NS - 1) % NS, nx < last ? nx : last);
+      }
       if (st < nst) {
-        const int buf = st & 1;
-        if (st + 1 < nst) load_a(st + 1);
-        if (st + PF - 1 < nst) MOE_LOAD_B((p + PF - 1) % PF, st + PF - 1);
+        const bf16 *abase = As + p * SLOT + lane * 8;
 #pragma unroll
         for (int sub = 0; sub < SUBS; ++sub) {
           bf16x8 bf[NB][NCB];
@@ -194,74 +230,115 @@ __global__ __launch_bounds__(256) void grouped_gemm(const GemmArgs g) {
                 bf[b][cb] = __builtin_bit_cast(bf16x8, bq[p][b][cb][sub]);
               }
             }
-          // A chunk: bf16 keeps k = 32*sub + 8*jq; FP4 uses k = 32*jq + 8*sub so
-          // that each lane's 32 weight codes share one scale.  Both operands
-          // use the same k order, so the products are unchanged.
-          const int ch = FP4 ? (4 * jq + sub) : (4 * sub + jq);
-          const bf16 *abase = &As[buf][r16 * BK + ((ch ^ (r16 & 7)) * 8)];
 #pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            if (m < nmb) {
-              const bf16x8 a = *(const bf16x8 *)(abase + m * 16 * BK);
+          for (int mc = 0; mc < MBE; mc += CH) {
+            bf16x8 a[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+              a[j] = *(const bf16x8 *)(abase + ((mc + j) * SUBS + sub) * FRAG);
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
 #pragma unroll
               for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb)
-                  acc[m][b][cb] =
-                      __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bf[b][cb], acc[m][b][cb], 0, 0, 0);
-            }
+                  acc[mc + j][b][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      a[j], bf[b][cb], acc[mc + j][b][cb], 0, 0, 0);
           }
         }
-        if (st + 1 < nst) store_a(buf ^ 1);
-        __syncthreads();
       }
     }
   }
-#undef MOE_LOAD_B
+#undef MOE_ISSUE
+  // drain the trailing copies before the workgroup's LDS can be reused
+  __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
 
   // ---- epilogue ----
   if constexpr (NB == 2) {
     const float L = g.limit;
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      if (m < nmb) {
+    for (int m = 0; m < MBE; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + jq * 4 + i;
-          if (row < rows) {
-            bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + jq * 4 + i;
+        if (row < rows) {
+          bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-              float gv = acc[m][0][cb][i], uv = acc[m][1][cb][i];
-              if (L > 0.f) {
-                gv = fminf(gv, L);
-                uv = fminf(fmaxf(uv, -L), L);
-              }
-              const float h = gv / (1.f + __expf(-gv)) * uv;
-              crow[cb * 16] = (bf16)h;
+          for (int cb = 0; cb < NCB; ++cb) {
+            float gv = acc[m][0][cb][i], uv = acc[m][1][cb][i];
+            if (L > 0.f) {
+              gv = fminf(gv, L);
+              uv = fminf(fmaxf(uv, -L), L);
             }
+            const float h = gv / (1.f + __expf(-gv)) * uv;
+            crow[cb * 16] = (bf16)h;
           }
         }
       }
-    }
   } else {
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      if (m < nmb) {
+    for (int m = 0; m < MBE; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m * 16 + jq * 4 + i;
-          if (row < rows) {
-            const int64_t R = row0 + row;
-            float wgt = 1.f;
-            if (R < g.routed_rows) wgt = g.route_w[(int64_t)g.sorted_tok[R] * g.k + g.sorted_slot[R]];
-            bf16 *crow = g.C + R * N + col0 + r16;
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + jq * 4 + i;
+        if (row < rows) {
+          bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) crow[cb * 16] = (bf16)(acc[m][0][cb][i] * wgt);
-          }
+          for (int cb = 0; cb < NCB; ++cb) crow[cb * 16] = (bf16)(acc[m][0][cb][i] * row_w[m][i]);
         }
       }
-    }
+  }
+}
+
+template <int WAVES, int NB, int NCB, int MB, bool FP4, int NS>
+constexpr int gemm_slot_elems() {
+  constexpr int SUBS = FP4 ? 4 : 2;
+  return ((MB * SUBS + WAVES - 1) / WAVES) * WAVES * 512;
+}
+
+// Grouped GEMM kernel: one workgroup per (tile, slab) work item; MB is the
+// tallest tile (in 16-row blocks) of this launch.
+template <int WAVES, int NB, int NCB, int MB, bool FP4, int NS>
+__global__ __launch_bounds__(WAVES * 64) void grouped_gemm(const GemmArgs g) {
+  constexpr int SLOT = gemm_slot_elems<WAVES, NB, NCB, MB, FP4, NS>();
+  __shared__ __attribute__((aligned(1024))) bf16 As[NS * SLOT];
+
+  // ---- work item (XCD-aware) ----
+  const int tend = g.tile_end >= 0 ? g.tile_end : *g.tile_count;
+  const int64_t work = (int64_t)(tend - g.tile_begin) * g.n_slabs;
+  const int xcd = blockIdx.x & 7;
+  const int64_t slot = blockIdx.x >> 3;
+  const int64_t per_xcd = (work + 7) >> 3;
+  if (slot >= per_xcd) return;
+  const int64_t item = xcd * per_xcd + slot;
+  if (item >= work) return;
+  const int tile = g.tile_begin + (int)(item / g.n_slabs);
+  const int slab = (int)(item - (int64_t)(tile - g.tile_begin) * g.n_slabs);
+
+  TileCtx t;
+  t.grp = g.tiles[4 * tile];
+  t.row0 = g.tiles[4 * tile + 1];
+  t.rows = g.tiles[4 * tile + 2];
+  t.shared = t.grp == g.E;
+  t.K = g.K;
+  t.N = g.N;
+  t.lane = threadIdx.x & 63;
+  t.wave = threadIdx.x >> 6;
+  t.col0 = slab * (WAVES * NCB * 16) + t.wave * NCB * 16;
+  const int nmb = (t.rows + 15) >> 4;
+
+  if constexpr (MB < MCH) {
+    gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT>(g, t, As);
+  } else {
+    const int nch = (nmb + MCH - 1) / MCH;
+    if (nch <= 1 || MB < 2 * MCH)
+      gemm_tile<WAVES, NB, NCB, (MB < MCH ? MB : MCH), FP4, NS, SLOT>(g, t, As);
+    else if (nch == 2 || MB < 3 * MCH)
+      gemm_tile<WAVES, NB, NCB, (MB < 2 * MCH ? MB : 2 * MCH), FP4, NS, SLOT>(g, t, As);
+    else if (nch == 3 || MB < 4 * MCH)
+      gemm_tile<WAVES, NB, NCB, (MB < 3 * MCH ? MB : 3 * MCH), FP4, NS, SLOT>(g, t, As);
+    else
+      gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT>(g, t, As);
   }
 }
 
@@ -379,24 +456,44 @@ int choose_tile_rows(const moe_config &cfg, int64_t T) {
   return 256;
 }
 
-template <int NB, int NCB, int MB, bool FP4, int PF>
+// Whether a configuration fits the hardware: the in-flight vector memory ops
+// must fit vmcnt's 6 bits and the copy ring the 160 KB of LDS.
+template <int WAVES, int NB, int NCB, int MB, bool FP4, int NS>
+constexpr bool gemm_cfg_fits() {
+  constexpr int SUBS = FP4 ? 4 : 2;
+  constexpr int NFW = (MB * SUBS + WAVES - 1) / WAVES;
+  constexpr int NBV = NB * NCB * (FP4 ? 2 : SUBS);
+  return (NS - 2) * (NFW + NBV) <= 63 && NS * NFW * WAVES * 1024 <= 160 * 1024;
+}
+
+template <int WAVES, int NB, int NCB, int MB, bool FP4, int NS>
 static hipError_t run_gemm(const GemmArgs &a, int max_tiles, hipStream_t s) {
+  if constexpr (!gemm_cfg_fits<WAVES, NB, NCB, MB, FP4, NS>()) {
+    return hipErrorInvalidValue;
+  } else {
   int64_t blocks = (int64_t)max_tiles * a.n_slabs;
   blocks = (blocks + 7) / 8 * 8;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm<NB, NCB, MB, FP4, PF>), dim3((unsigned)blocks), dim3(256), 0,
-                     s, a);
+  hipLaunchKernelGGL((grouped_gemm<WAVES, NB, NCB, MB, FP4, NS>), dim3((unsigned)blocks),
+                     dim3(WAVES * 64), 0, s, a);
   return hipGetLastError();
+  }
 }
 
-template <int NB, int NCB, bool FP4, int PF>
+// Launch configuration: waves per workgroup, 16-column blocks per wave and
+// matrix, pipeline depth.  Chosen per (matrix count, weight format, tile
+// height) from sweeps on MI355X at the V3 prefill / decode, hash and
+// V4.1-Flash shapes; the first entry whose column slab divides N is used.
+struct GemmCfg { int waves, ncb, ns; };
+
+template <int WAVES, int NB, int NCB, bool FP4, int NS>
 static hipError_t run_gemm_mb(int mb, const GemmArgs &a, int max_tiles, hipStream_t s) {
   switch (mb) {
-    case 1: return run_gemm<NB, NCB, 1, FP4, PF>(a, max_tiles, s);
-    case 4: return run_gemm<NB, NCB, 4, FP4, PF>(a, max_tiles, s);
-    case 8: return run_gemm<NB, NCB, 8, FP4, PF>(a, max_tiles, s);
-    case 12: return run_gemm<NB, NCB, 12, FP4, PF>(a, max_tiles, s);
-    case 16: return run_gemm<NB, NCB, 16, FP4, PF>(a, max_tiles, s);
+    case 1: return run_gemm<WAVES, NB, NCB, 1, FP4, NS>(a, max_tiles, s);
+    case 4: return run_gemm<WAVES, NB, NCB, 4, FP4, NS>(a, max_tiles, s);
+    case 8: return run_gemm<WAVES, NB, NCB, 8, FP4, NS>(a, max_tiles, s);
+    case 12: return run_gemm<WAVES, NB, NCB, 12, FP4, NS>(a, max_tiles, s);
+    case 16: return run_gemm<WAVES, NB, NCB, 16, FP4, NS>(a, max_tiles, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -404,18 +501,36 @@ static hipError_t run_gemm_mb(int mb, const GemmArgs &a, int max_tiles, hipStrea
 // One grouped GEMM launch over a tile range.
 static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tiles,
                               hipStream_t s) {
-  const int ncb = (a.N % 128 == 0 && mb <= 1) ? 2 : 1;
-  a.n_slabs = a.N / (4 * ncb * 16);
-  if (fp4) {
-    if (nb == 2) return run_gemm_mb<2, 1, true, 2>(mb, a, max_tiles, s);
-    return run_gemm_mb<1, 1, true, 2>(mb, a, max_tiles, s);
+  const bool decode = mb == 1;
+#define MOE_TRY(W, NB_, NCB, FP4_, NS)                                          \
+  if (a.N % ((W) * (NCB) * 16) == 0) {                                          \
+    a.n_slabs = a.N / ((W) * (NCB) * 16);                                       \
+    return run_gemm_mb<W, NB_, NCB, FP4_, NS>(mb, a, max_tiles, s);             \
   }
-  if (ncb == 2) {
-    if (nb == 2) return run_gemm_mb<2, 2, false, 4>(mb, a, max_tiles, s);
-    return run_gemm_mb<1, 2, false, 4>(mb, a, max_tiles, s);
+  if (nb == 2) {
+    if (fp4) {
+      if (decode) { MOE_TRY(4, 2, 2, true, 3) }
+      else { MOE_TRY(4, 2, 2, true, 2) }
+      MOE_TRY(4, 2, 1, true, 2)
+    } else {
+      if (decode) { MOE_TRY(4, 2, 2, false, 4) }
+      else { MOE_TRY(8, 2, 1, false, 3) }
+      MOE_TRY(4, 2, 1, false, 3)
+    }
+  } else {
+    if (fp4) {
+      if (decode) { MOE_TRY(4, 1, 4, true, 3) }
+      else { MOE_TRY(4, 1, 4, true, 2) }
+      MOE_TRY(4, 1, 1, true, 2)
+    } else {
+      if (decode) { MOE_TRY(4, 1, 4, false, 4) }
+      else if (mb >= 16) { MOE_TRY(8, 1, 1, false, 4) }
+      else { MOE_TRY(4, 1, 4, false, 3) }
+      MOE_TRY(4, 1, 1, false, 3)
+    }
   }
-  if (nb == 2) return run_gemm_mb<2, 1, false, 3>(mb, a, max_tiles, s);
-  return run_gemm_mb<1, 1, false, 3>(mb, a, max_tiles, s);
+#undef MOE_TRY
+  return hipErrorInvalidValue;
 }
 
 static hipError_t mark(const ExpertPlan &p, int i, hipStream_t s) {
@@ -457,11 +572,8 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   a.E = p.E;
   a.tiles = p.tiles;
   a.tile_count = p.tile_count;
-  a.k = p.k;
   a.routed_rows = routed_rows;
-  a.sorted_tok = p.sorted_tok;
-  a.sorted_slot = p.sorted_slot;
-  a.route_w = p.route_w;
+  a.sorted_w = p.sorted_w;
 
   // GEMM1: gate|up + SwiGLU -> H
   a.A = (const bf16 *)p.x;

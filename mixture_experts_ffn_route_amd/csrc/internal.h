@@ -25,6 +25,8 @@ struct TileSpec {
   int tile_rows;         // rows per tile (BM)
   int n_shared_tiles;    // shared-expert tiles, stored first
   int32_t *shared_rows_tok;  // sorted_tok + T*k: identity rows for the shared expert
+  const float *route_w;      // [T, k] gate values, or null
+  float *sorted_w;           // [T*k]  gate value of each permuted row, or null
 };
 
 hipError_t launch_permute(int E, int k, int64_t T, const int32_t *indices, int32_t *counts,
@@ -46,6 +48,7 @@ struct ExpertPlan {
   const float *route_w;
   const int32_t *route_idx, *offsets;
   const int32_t *sorted_tok, *sorted_slot, *inverse;
+  const float *sorted_w;
   const int32_t *tiles, *tile_count;
   int max_tiles, tile_rows, n_shared_tiles;
   void *h, *yrows, *y;

@@ -90,6 +90,7 @@ int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
   l.offsets = take(sizeof(int32_t) * (E + 1));
   l.sorted_tok = take(sizeof(int32_t) * (T * k + T));
   l.sorted_slot = take(sizeof(int32_t) * T * k);
+  l.sorted_weight = take(sizeof(float) * T * k);
   l.inverse = take(sizeof(int32_t) * T * k);
   l.tiles = take(sizeof(int32_t) * 4 * max_tiles);
   l.tile_count = take(sizeof(int32_t));
@@ -234,6 +235,7 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   int32_t *offsets = (int32_t *)(base + L.offsets);
   int32_t *sorted_tok = (int32_t *)(base + L.sorted_tok);
   int32_t *sorted_slot = (int32_t *)(base + L.sorted_slot);
+  float *sorted_w = (float *)(base + L.sorted_weight);
   int32_t *inverse = (int32_t *)(base + L.inverse);
   int32_t *tiles = (int32_t *)(base + L.tiles);
   int32_t *tile_count = (int32_t *)(base + L.tile_count);
@@ -257,6 +259,8 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   ts.tile_rows = L.tile_rows;
   ts.n_shared_tiles = cfg->n_shared_experts ? (int)((T + L.tile_rows - 1) / L.tile_rows) : 0;
   ts.shared_rows_tok = sorted_tok + T * k;
+  ts.route_w = route_w;
+  ts.sorted_w = sorted_w;
   if (events && hipEventRecord(events[MOE_STAGE_PERMUTE], s) != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_permute(cfg->n_routed_experts, k, T, route_idx, counts, offsets, sorted_tok,
                           sorted_slot, inverse, flags, &ts, /*clear_flags=*/!hash, s);
@@ -279,6 +283,7 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   p.offsets = offsets;
   p.sorted_tok = sorted_tok;
   p.sorted_slot = sorted_slot;
+  p.sorted_w = sorted_w;
   p.inverse = inverse;
   p.tiles = tiles;
   p.tile_count = tile_count;

@@ -31,6 +31,8 @@ struct PermuteArgs {
   int32_t *counts, *offsets, *sorted_tok, *sorted_slot, *inverse;
   uint32_t *flags;
   int32_t *tiles, *tile_count, *shared_rows_tok;
+  const float *route_w;
+  float *sorted_w;
   int tile_rows, n_shared_tiles;
   int clear_flags;      // zero flags[0] before use (nothing earlier in the call set it)
 };
@@ -159,6 +161,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const PermuteArgs
       a.sorted_tok[dest] = (int32_t)t;
       a.sorted_slot[dest] = (int32_t)(p - t * a.k);
       a.inverse[p] = dest;
+      if (a.sorted_w) a.sorted_w[dest] = a.route_w[p];
       if (rank == cnt - 1) hist[w * E + e] = row0 + cnt;
     }
   }
@@ -185,6 +188,8 @@ hipError_t launch_permute(int E, int k, int64_t T, const int32_t *indices, int32
   a.shared_rows_tok = tiles ? tiles->shared_rows_tok : nullptr;
   a.tile_rows = tiles ? tiles->tile_rows : 1;
   a.n_shared_tiles = tiles ? tiles->n_shared_tiles : 0;
+  a.route_w = tiles ? tiles->route_w : nullptr;
+  a.sorted_w = tiles && tiles->route_w ? tiles->sorted_w : nullptr;
   const size_t lds = ((size_t)kPermWaves * E + kPermWaves + 1) * sizeof(int);
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute((const void *)permute_kernel,

@@ -127,6 +127,7 @@ def test_workspace_layout_is_aligned_and_disjoint():
         es = 4 if cfg.act_dtype == "f32" else 2
         sizes = {"route_weights": 4 * T * k, "route_indices": 4 * T * k, "counts": 4 * E,
                  "offsets": 4 * (E + 1), "sorted_tok": 4 * (T * k + T), "sorted_slot": 4 * T * k,
+                 "sorted_weight": 4 * T * k,
                  "inverse": 4 * T * k, "tiles": 16 * lay["max_tiles"], "tile_count": 4, "flags": 16,
                  "h": es * rows * cfg.moe_inter_dim, "yrows": es * rows * cfg.dim}
         spans = sorted((lay[n], lay[n] + s) for n, s in sizes.items())
