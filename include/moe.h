@@ -146,8 +146,7 @@ const char *moe_status_string(int status);
  * MOE_ERR_INVALID_ARG for inconsistent fields (E % G, k > E,
  * n_limited_groups > G, k > n_limited_groups * E / G, bad enums, ...) or
  * MOE_ERR_UNSUPPORTED for shapes this build does not implement (bf16/FP4
- * paths need dim % 64 == 0 and I % 64 == 0, FP4 dim % 128 == 0 and
- * I % 128 == 0; group ranges whose size over
+ * paths need dim % 64 == 0 and I % 64 == 0; group ranges whose size over
  * ceil(E/64) is not a power of two). */
 int moe_validate_config(const moe_config *cfg);
 

@@ -106,6 +106,10 @@ SMALL_WORKLOADS = {
         "fp4_small",
         replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48),
         T=157),
+    "fp4_odd_widths": Workload(
+        "fp4_odd_widths",
+        replace(V41_FLASH_FP4.cfg, dim=320, moe_inter_dim=192, n_routed_experts=48),
+        T=77),
     "fp4_clamp_small": Workload(
         "fp4_clamp_small",
         replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48),

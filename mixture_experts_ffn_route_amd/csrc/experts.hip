@@ -13,13 +13,14 @@
 // of one expert (or of the shared expert), a slab WAVES*NCB*16 output
 // columns of each weight matrix.  The weight slab is streamed from HBM
 // exactly once per tile -- one tile normally holds all rows of an expert, so
-// the routed weights are read once per forward -- straight into registers
-// in the MFMA operand layout (no LDS hop for the streamed operand) with a
-// PF-1 stage prefetch ring.  The gathered activation rows are staged through
-// a double-buffered, XOR-swizzled LDS tile shared by the four waves.  MFMA
-// is v_mfma_f32_16x16x32_bf16 (fp32 accumulate).  FP4 weights are loaded as
-// 32 codes + one E8M0 scale per lane per 128-deep stage and expanded to bf16
-// in registers with v_cvt_scalef32_pk_bf16_fp4.
+// the routed weights are read once per forward -- straight into registers in
+// the MFMA operand layout, through an NS-deep register ring.  The gathered
+// activation rows travel global -> LDS through asynchronous copies
+// (global_load_lds_dwordx4) that land directly in the MFMA A-operand layout,
+// in an NS-deep LDS ring shared by the waves.  MFMA is
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  FP4 weights are loaded
+// as 16 codes + one E8M0 scale per lane per 64-input stage and expanded to
+// bf16 in registers with v_cvt_scalef32_pk_bf16_fp4.
 //
 // The workgroup -> work item map is XCD aware: consecutive workgroups land on
 // different XCDs, so each XCD is given a contiguous range of items (all
@@ -90,19 +91,23 @@ struct TileCtx {
 // per stage.
 template <int WAVES, int NB, int NCB, int MBE, bool FP4, int NS, int SLOT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, bf16 *As) {
-  constexpr int BK = FP4 ? 128 : 64;       // inputs per stage
+  constexpr int BK = 64;                   // inputs per stage
   constexpr int SUBS = BK / 32;            // MFMA k-steps per stage
   constexpr int FRAG = 512;                // bf16 per 16x32 A fragment (1 KB)
   constexpr int NFRAG = MBE * SUBS;        // A fragments per stage
   constexpr int NFW = (NFRAG + WAVES - 1) / WAVES;
-  constexpr int NQ = FP4 ? 1 : SUBS;       // 16-byte weight loads per (matrix, block) per stage
-  constexpr int NBV = NB * NCB * (FP4 ? 2 : NQ);   // weight-side vector memory ops per stage
+  constexpr int NQ = SUBS;                 // bf16: 16-byte weight loads per (matrix, block) per stage
+  // weight-side vector memory ops per stage: bf16 one 16-byte load per k-step;
+  // FP4 one 8-byte load (16 codes) plus one scale byte
+  constexpr int NBV = NB * NCB * (FP4 ? 2 : NQ);
   constexpr int VM_PER_STAGE = NFW + NBV;          // every wave issues exactly this many
   constexpr int CH = MBE < MCH ? MBE : MCH;
   static_assert(NS >= 2, "pipeline needs two stages");
   static_assert((NS - 2) * VM_PER_STAGE <= 63, "vmcnt holds 6 bits");
   static_assert(NFW * WAVES * FRAG <= SLOT, "ring slot too small");
   static_assert(MBE % CH == 0, "row blocks come in whole chunks");
+  // refill ops issued after each MFMA chunk (all of them land within the stage)
+  constexpr int ISSUE_PER_CHUNK = (VM_PER_STAGE + SUBS * (MBE / CH) - 1) / (SUBS * (MBE / CH));
 
   const int lane = t.lane, wave = t.wave, r16 = lane & 15, jq = lane >> 4;
   const int K = t.K, N = t.N, rows = t.rows, row0 = t.row0, col0 = t.col0;
@@ -135,9 +140,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
     int r = m * 16 + r16;
     r = r < rows ? r : rows - 1;
     const int64_t src = g.a_rows ? g.a_rows[row0 + r] : (int64_t)(row0 + r);
-    // bf16 keeps k = 32s + 8jq; FP4 uses k = 32jq + 8s so that each lane's 32
-    // weight codes share one scale.  A and B use the same order.
-    const int koff = FP4 ? (32 * jq + 8 * s) : (32 * s + 8 * jq);
+    // bf16 keeps k = 32s + 8jq; FP4 uses k = 16jq + 8s so that each lane's 16
+    // weight codes of a stage lie in one 32-input scale block.  A and B use
+    // the same order, so the products are unchanged.
+    const int koff = FP4 ? (16 * jq + 8 * s) : (32 * s + 8 * jq);
     asrc[i] = g.A + src * K + koff;
   }
 
@@ -151,8 +157,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
       const int64_t n = col0 + cb * 16 + r16;
       if constexpr (FP4) {
         const int64_t K2 = K / 2, K32 = K / 32;
-        bptr[b][cb] = (const uint8_t *)g.B[b] + ((int64_t)t.grp * N + n) * K2 + jq * 16;
-        sptr[b][cb] = g.S[b] + ((int64_t)t.grp * N + n) * K32 + jq;
+        bptr[b][cb] = (const uint8_t *)g.B[b] + ((int64_t)t.grp * N + n) * K2 + jq * 8;
+        sptr[b][cb] = g.S[b] + ((int64_t)t.grp * N + n) * K32 + (jq >> 1);
       } else {
         const bf16 *base = t.shared ? g.SB[b] : (const bf16 *)g.B[b] + (int64_t)t.grp * N * K;
         bptr[b][cb] = (const uint8_t *)(base + n * K + jq * 8);
@@ -168,32 +174,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[m][b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 bq[NS][NB][NCB][NQ];
-  uint32_t sq[NS][NB][NCB];
+  u32x4 bq[NS][NB][NCB][FP4 ? 1 : NQ];   // bf16 weight fragments
+  uint2 fq[NS][NB][NCB];                 // FP4 codes (16 per lane per stage)
+  uint32_t sq[NS][NB][NCB];              // FP4 scale bytes
   const int nst = K / BK;
 
-#define MOE_ISSUE(SLOTI, ST)                                                              \
-  {                                                                                       \
-    _Pragma("unroll") for (int i = 0; i < NFW; ++i)                                       \
-      dma16(asrc[i] + (int64_t)(ST) * BK, As + (SLOTI) * SLOT + (wave + WAVES * i) * FRAG); \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                        \
-    _Pragma("unroll") for (int cb = 0; cb < NCB; ++cb) {                                  \
-      if constexpr (FP4) {                                                                \
-        bq[SLOTI][b][cb][0] = *(const u32x4 *)(bptr[b][cb] + (int64_t)(ST) * (BK / 2));   \
-        sq[SLOTI][b][cb] = sptr[b][cb][(ST) * (BK / 32)];                                 \
-      } else {                                                                            \
-        _Pragma("unroll") for (int q = 0; q < NQ; ++q)                                    \
-          bq[SLOTI][b][cb][q] =                                                           \
-              *(const u32x4 *)(bptr[b][cb] + ((int64_t)(ST) * BK + q * 32) * 2);          \
-      }                                                                                   \
-    }                                                                                     \
-  }
+  // Issue the q-th vector memory op of stage ST into ring slot SL (ops
+  // 0..NFW-1: activation copies; then the weight loads).  Called with
+  // indices that are constants after unrolling, so the branches fold.
+  auto issue_op = [&](int SL, int ST, int q) {
+    if (q < NFW) {
+      dma16(asrc[q] + (int64_t)ST * BK, As + SL * SLOT + (wave + WAVES * q) * FRAG);
+    } else if constexpr (FP4) {
+      const int r = q - NFW, bc = r >> 1, b = bc / NCB, cb = bc - b * NCB;
+      if ((r & 1) == 0)
+        fq[SL][b][cb] = *(const uint2 *)(bptr[b][cb] + (int64_t)ST * (BK / 2));
+      else
+        sq[SL][b][cb] = sptr[b][cb][ST * (BK / 32)];
+    } else {
+      const int r = q - NFW, bc = r / NQ, qq = r - bc * NQ, b = bc / NCB, cb = bc - b * NCB;
+      bq[SL][b][cb][qq] = *(const u32x4 *)(bptr[b][cb] + ((int64_t)ST * BK + qq * 32) * 2);
+    }
+  };
+  auto issue_stage = [&](int SL, int ST) {
+#pragma unroll
+    for (int q = 0; q < VM_PER_STAGE; ++q) issue_op(SL, ST, q);
+  };
 
   // prologue: stages 0 .. NS-2 (stage indices past the end re-read the
   // last stage: same addresses, so they hit in L2 and cost no HBM bytes)
   const int last = nst - 1;
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) MOE_ISSUE(p, p < last ? p : last);
+  for (int p = 0; p < NS - 1; ++p) issue_stage(p, p < last ? p : last);
 
   // Every iteration issues exactly one stage of loads per step, so the number
   // of vector memory ops between a stage's issue and its use is the constant
@@ -205,10 +217,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
       // stages st+1 .. st+NS-2 may stay in flight
       __builtin_amdgcn_s_waitcnt(MOE_VMCNT((NS - 2) * VM_PER_STAGE));
       __builtin_amdgcn_s_barrier();     // every wave's copies for st landed; st-1 fully read
-      {
-        const int nx = st + NS - 1;
-        MOE_ISSUE((p + NS - 1) % NS, nx < last ? nx : last);
-      }
+      // the refill of the slot freed by stage st-1 (stage st+NS-1) is spread
+      // over this stage's MFMA chunks, so a load that waits for queue space
+      // stalls the wave while issued MFMAs keep the matrix unit busy
+      const int nslot = (p + NS - 1) % NS;
+      const int nx = st + NS - 1 < last ? st + NS - 1 : last;
+      if (st >= nst) issue_stage(nslot, nx);
       if (st < nst) {
         const bf16 *abase = As + p * SLOT + lane * 8;
 #pragma unroll
@@ -219,7 +233,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
               if constexpr (FP4) {
-                const unsigned word = bq[p][b][cb][0][sub];
+                const unsigned word = sub == 0 ? fq[p][b][cb].x : fq[p][b][cb].y;
                 const float scale = __uint_as_float(sq[p][b][cb] << 23);
                 const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
                 const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
@@ -244,6 +258,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
                 for (int cb = 0; cb < NCB; ++cb)
                   acc[mc + j][b][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                       a[j], bf[b][cb], acc[mc + j][b][cb], 0, 0, 0);
+            const int chunk = sub * (MBE / CH) + mc / CH;
+#pragma unroll
+            for (int j = 0; j < ISSUE_PER_CHUNK; ++j) {
+              const int q = chunk * ISSUE_PER_CHUNK + j;
+              if (q < VM_PER_STAGE) issue_op(nslot, nx, q);
+            }
           }
         }
       }
@@ -292,14 +312,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
 
 template <int WAVES, int NB, int NCB, int MB, bool FP4, int NS>
 constexpr int gemm_slot_elems() {
-  constexpr int SUBS = FP4 ? 4 : 2;
+  constexpr int SUBS = 2;
   return ((MB * SUBS + WAVES - 1) / WAVES) * WAVES * 512;
 }
 
 // Grouped GEMM kernel: one workgroup per (tile, slab) work item; MB is the
 // tallest tile (in 16-row blocks) of this launch.
+// Waves per SIMD the kernel is scheduled for: the tall tiles keep their
+// accumulators in one wave per SIMD (the compiler then spends registers on
+// latency hiding instead of chasing occupancy it cannot reach); the short
+// decode tiles and 8-wave workgroups run two per SIMD.
+template <int WAVES, int MB>
+constexpr int gemm_waves_per_simd() { return (MB >= 8 && WAVES == 4) ? 1 : 2; }
+
 template <int WAVES, int NB, int NCB, int MB, bool FP4, int NS>
-__global__ __launch_bounds__(WAVES * 64) void grouped_gemm(const GemmArgs g) {
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(gemm_waves_per_simd<WAVES, MB>(),
+                                   gemm_waves_per_simd<WAVES, MB>())))
+void grouped_gemm(const GemmArgs g) {
   constexpr int SLOT = gemm_slot_elems<WAVES, NB, NCB, MB, FP4, NS>();
   __shared__ __attribute__((aligned(1024))) bf16 As[NS * SLOT];
 
@@ -460,9 +490,9 @@ int choose_tile_rows(const moe_config &cfg, int64_t T) {
 // must fit vmcnt's 6 bits and the copy ring the 160 KB of LDS.
 template <int WAVES, int NB, int NCB, int MB, bool FP4, int NS>
 constexpr bool gemm_cfg_fits() {
-  constexpr int SUBS = FP4 ? 4 : 2;
+  constexpr int SUBS = 2;
   constexpr int NFW = (MB * SUBS + WAVES - 1) / WAVES;
-  constexpr int NBV = NB * NCB * (FP4 ? 2 : SUBS);
+  constexpr int NBV = NB * NCB * 2;
   return (NS - 2) * (NFW + NBV) <= 63 && NS * NFW * WAVES * 1024 <= 160 * 1024;
 }
 
@@ -509,9 +539,9 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
   }
   if (nb == 2) {
     if (fp4) {
-      if (decode) { MOE_TRY(4, 2, 2, true, 3) }
-      else { MOE_TRY(4, 2, 2, true, 2) }
-      MOE_TRY(4, 2, 1, true, 2)
+      if (decode) { MOE_TRY(4, 2, 2, true, 4) }
+      else { MOE_TRY(4, 2, 2, true, 3) }
+      MOE_TRY(4, 2, 1, true, 3)
     } else {
       if (decode) { MOE_TRY(4, 2, 2, false, 4) }
       else { MOE_TRY(8, 2, 1, false, 3) }
@@ -519,9 +549,9 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
     }
   } else {
     if (fp4) {
-      if (decode) { MOE_TRY(4, 1, 4, true, 3) }
-      else { MOE_TRY(4, 1, 4, true, 2) }
-      MOE_TRY(4, 1, 1, true, 2)
+      if (decode) { MOE_TRY(4, 1, 4, true, 4) }
+      else { MOE_TRY(4, 1, 4, true, 3) }
+      MOE_TRY(4, 1, 1, true, 3)
     } else {
       if (decode) { MOE_TRY(4, 1, 4, false, 4) }
       else if (mb >= 16) { MOE_TRY(8, 1, 1, false, 4) }

@@ -44,9 +44,6 @@ int validate(const moe_config *c) {
     if (c->expert_dtype != MOE_DTYPE_BF16 && c->expert_dtype != MOE_DTYPE_FP4_E2M1)
       return MOE_ERR_INVALID_ARG;
     if (c->dim % 64 != 0 || c->moe_inter_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
-    // FP4 weights are consumed 128 inputs (four 32-blocks) per stage
-    if (c->expert_dtype == MOE_DTYPE_FP4_E2M1 && (c->dim % 128 != 0 || c->moe_inter_dim % 128 != 0))
-      return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_INVALID_ARG;
   }

@@ -62,7 +62,7 @@ BAD = [
     ("fp32 act with bf16 experts", replace(V3, act_dtype="f32"), B.MOE_ERR_INVALID_ARG),
     ("hash without vocab", replace(C.HASH_BF16.cfg, vocab_size=0), B.MOE_ERR_INVALID_ARG),
     ("bf16 dim % 64", replace(V3, dim=7168 + 32), B.MOE_ERR_UNSUPPORTED),
-    ("fp4 dim % 128", replace(C.V41_FLASH_FP4.cfg, dim=5120 + 64), B.MOE_ERR_UNSUPPORTED),
+    ("fp4 dim % 64", replace(C.V41_FLASH_FP4.cfg, dim=5120 + 32), B.MOE_ERR_UNSUPPORTED),
     ("two shared experts", replace(V3, n_shared_experts=2), B.MOE_ERR_UNSUPPORTED),
     ("k > 16", replace(V3, n_activated_experts=17, n_limited_groups=8), B.MOE_ERR_UNSUPPORTED),
     ("learned E > 512", replace(V3, n_routed_experts=1024, n_expert_groups=1, n_limited_groups=1), B.MOE_ERR_UNSUPPORTED),
