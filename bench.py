@@ -170,7 +170,8 @@ def cpu_baseline(wl, layer, sample_tokens):
                                         n_groups=cfg.n_expert_groups,
                                         topk_groups=cfg.n_limited_groups,
                                         topk=cfg.n_activated_experts, route_scale=cfg.route_scale)
-    # host copies of the experts the sample touches (data staging, untimed)
+    # host copies of the experts the sample touches, in their stored format
+    # (data staging, untimed; the widening to float64 is the oracle's work)
     host = {}
     for e in np.unique(idx):
         e = int(e)
@@ -178,15 +179,15 @@ def cpu_baseline(wl, layer, sample_tokens):
             host[e] = tuple((layer[n][e].cpu().numpy(), layer["s_" + n[2:]][e].cpu().numpy())
                             for n in ("w_gate", "w_up", "w_down"))
         else:
-            host[e] = tuple(f32(layer[n][e]) for n in ("w_gate", "w_up", "w_down"))
+            host[e] = tuple(layer[n][e].cpu() for n in ("w_gate", "w_up", "w_down"))
     shared = None
     if cfg.n_shared_experts:
-        shared_host = tuple(f32(layer[n]) for n in ("sh_gate", "sh_up", "sh_down"))
+        shared_host = tuple(layer[n].cpu() for n in ("sh_gate", "sh_up", "sh_down"))
 
     def expert(e):
         if cfg.expert_dtype == "fp4":
             return tuple(oracle.fp4_decode(p, s) for p, s in host[e])
-        return tuple(a.astype(np.float64) for a in host[e])
+        return tuple(a.double().numpy() for a in host[e])
 
     t0 = time.perf_counter()
     if cfg.route_mode == "hash":
@@ -198,10 +199,10 @@ def cpu_baseline(wl, layer, sample_tokens):
                                         topk=cfg.n_activated_experts, route_scale=cfg.route_scale)
     oracle.permute(idx, cfg.n_routed_experts)
     if cfg.n_shared_experts:
-        shared = tuple(a.astype(np.float64) for a in shared_host)
+        shared = tuple(a.double().numpy() for a in shared_host)
     oracle.layer_forward(x, w, idx, expert, shared, cfg.swiglu_limit)
     dt = time.perf_counter() - t0
-    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [torch.get_num_threads()])
     return {"value": round(S / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of the {wl.T} tokens of {wl.name}: route + permute + routed and "
                       f"shared SwiGLU in float64 ({len(host)} experts touched), {dt:.1f} s"}
@@ -215,7 +216,8 @@ def main():
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode", default="v3_decode", help="second workload ('' to skip)")
     ap.add_argument("--extra", default="", help="comma-separated extra workloads to report")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=96,
+                    help="tokens of the batch the CPU oracle is timed on (about 10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (reference "
