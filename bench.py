@@ -99,8 +99,17 @@ def build_layer(wl, dev, B, synth):
     return layer
 
 
-def time_workload(wl, layer, steps, warmup, B, torch):
-    cfg, T = wl.cfg, wl.T
+def run_weights(wl, layer, B, layout):
+    """(config, layer) the timed steps use: the expert matrices rewritten once
+    into the tiled layout (a load-time storage format) unless `layout` is
+    "rows" or the layer is fp32."""
+    if layout == "rows" or wl.cfg.act_dtype != "bf16":
+        return wl.cfg, layer
+    return B.pack_layer(wl.cfg, layer)
+
+
+def time_workload(wl, layer, steps, warmup, B, torch, cfg=None):
+    cfg, T = (cfg or wl.cfg), wl.T
     dev = layer["x"].device
     ws = B.alloc_workspace(cfg, T, dev)
     y = torch.empty_like(layer["x"])
@@ -215,10 +224,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode", default="v3_decode", help="second workload ('' to skip)")
-    ap.add_argument("--extra", default="", help="comma-separated extra workloads to report")
+    ap.add_argument("--extra", default="hash_bf16,v41_flash_fp4,tiny_fp32",
+                    help="comma-separated further workloads to report ('' for none)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=96,
                     help="tokens of the batch the CPU oracle is timed on (about 10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
+                    help="expert weight storage the timed steps read (tiled: packed once by "
+                         "moe_pack_weights before timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -254,7 +267,9 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t:.1f} s; timing {args.steps} steps after {args.warmup} warmup")
     peak = MFMA_PEAK_TFLOPS[wl.cfg.expert_dtype if wl.cfg.expert_dtype == "fp4" else wl.cfg.act_dtype]
-    ms, stage_ms, counts = time_workload(wl, layer, args.steps, args.warmup, B, torch)
+    rcfg, rlayer = run_weights(wl, layer, B, args.layout)
+    torch.cuda.synchronize()
+    ms, stage_ms, counts = time_workload(wl, rlayer, args.steps, args.warmup, B, torch, rcfg)
     rep = workload_report(wl, ms, stage_ms, counts, peak)
     log(f"{wl.name}: {rep['ms_per_step']} ms/step, {rep['tokens_per_s']} tokens/s, stages {rep['stage_ms']}")
 
@@ -276,6 +291,7 @@ def main():
                    "n_activated_experts": wl.cfg.n_activated_experts,
                    "moe_inter_dim": wl.cfg.moe_inter_dim,
                    "n_shared_experts": wl.cfg.n_shared_experts,
+                   "weight_layout": rcfg.weight_layout,
                    "parallelism": "single-gpu (all experts resident)"},
     }
     g1 = rep["gemm1"]
@@ -293,20 +309,20 @@ def main():
         w2 = C.FULL_WORKLOADS[name]
         if w2.cfg == wl.cfg and w2.seed == wl.seed and max(w2.T, w2.x_rows) == wl.T:
             # same layer and weights; x is the first T rows of the same draw
-            l2 = dict(layer)
+            l2 = dict(rlayer)
             l2["x"] = layer["x"][:w2.T].contiguous()
+            c2cfg = rcfg
         else:
             log(f"generating {name} inputs")
-            l2 = build_layer(w2, dev, B, synth)
+            c2cfg, l2 = run_weights(w2, build_layer(w2, dev, B, synth), B, args.layout)
         p2 = MFMA_PEAK_TFLOPS[w2.cfg.expert_dtype if w2.cfg.expert_dtype == "fp4" else w2.cfg.act_dtype]
-        ms2, st2, c2 = time_workload(w2, l2, args.steps, args.warmup, B, torch)
+        ms2, st2, c2 = time_workload(w2, l2, args.steps, args.warmup, B, torch, c2cfg)
         r2 = workload_report(w2, ms2, st2, c2, p2)
         r2["roofline"] = {k: r2["gemm1"][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
         r2["roofline"]["traffic"] = load_traffic(name)
         reports[name] = r2
         log(f"{name}: {r2['ms_per_step']} ms/step, {r2['tokens_per_s']} tokens/s, stages {r2['stage_ms']}")
-        if l2 is not layer:
-            del l2
+        del l2
     if args.decode:
         out["decode"] = {"workload": args.decode, **reports.pop(args.decode)}
     if reports:

@@ -30,6 +30,9 @@
  *   - Weight matrices are [out, in] row-major with the input (K) dimension
  *     contiguous, like nn.Linear: gate weight [E, dim]; routed W_gate and
  *     W_up [E, I, dim]; W_down [E, dim, I]; shared [I, dim], [I, dim], [dim, I].
+ *     Routed and shared expert matrices (and FP4 scales) may instead be
+ *     given in the tiled layout that moe_pack_weights writes
+ *     (moe_config.weight_layout = MOE_LAYOUT_TILED); same sizes, same values.
  *   - bf16 is IEEE-style bfloat16 (upper half of an fp32); fp32 is IEEE.
  *   - FP4 routed experts (MOE_DTYPE_FP4_E2M1): E2M1 codes packed two per
  *     byte along the input dimension, element 2i in the low nibble; one
@@ -73,6 +76,11 @@ typedef enum {
   MOE_DTYPE_FP4_E2M1 = 2      /* routed experts only; see conventions above    */
 } moe_dtype;
 
+typedef enum {
+  MOE_LAYOUT_ROWS = 0,        /* expert matrices [out, in] row-major           */
+  MOE_LAYOUT_TILED = 1        /* expert matrices as written by moe_pack_weights */
+} moe_weight_layout;
+
 /* Layer configuration.  Field names follow the model arguments of the
  * "gate-init" excerpt and the V4.1 MoE class. */
 typedef struct {
@@ -92,6 +100,8 @@ typedef struct {
   int32_t act_dtype;           /* x, y, gate weight, shared expert: F32 or BF16  */
   int32_t expert_dtype;        /* routed experts: F32 (act F32), BF16 or
                                   FP4_E2M1 (act BF16)                            */
+  int32_t weight_layout;       /* moe_weight_layout of the routed and shared
+                                  expert matrices; TILED needs act_dtype BF16    */
 } moe_config;
 
 /* Layer weights; unused members may be NULL. */
@@ -164,6 +174,31 @@ int moe_validate_config(const moe_config *cfg);
 int moe_build_tid2eid(const double *p, int64_t m, int32_t n, int32_t k,
                       int32_t *tid2eid, double *load,
                       double *max_vio, double *min_vio);
+
+/* Rewrite the expert matrices into the tiled layout the grouped GEMMs
+ * stream contiguously (a storage format only: the tiled matrices hold the same
+ * values, and moe_forward gives bit-identical results with either layout).
+ * Done once when the weights are loaded, not per forward call.
+ *   src  expert matrices in MOE_LAYOUT_ROWS (cfg->weight_layout is ignored):
+ *        w_gate, w_up, w_down, the FP4 scales and the shared matrices; NULL
+ *        members are skipped.  gate_w, gate_bias and tid2eid are not touched.
+ *   dst  caller-allocated buffers of the same byte sizes for every non-NULL
+ *        src member (the pointers are written through; dst's struct itself is
+ *        read-only), not overlapping src.
+ * Layout, for a matrix [N, K] of one expert (K = input dim; N, K % 64 == 0):
+ *   bf16: 16 x 32 tiles, tile (n/16, k/32) at element ((n/16)*(K/32) + k/32)*512;
+ *         inside a tile, element (n, k) at (((k%32)/8)*16 + n%16)*8 + k%8 (one
+ *         16-byte group per MFMA lane: 16 outputs x 8 consecutive inputs).
+ *   FP4 codes (bytes [N, K/2]): 16 x 64-input tiles of 512 bytes, tile
+ *         (n/16, kb/32) at byte ((n/16)*(K/64) + kb/32)*512 for byte column kb;
+ *         inside, byte (n, kb) at (((kb%32)/8)*16 + n%16)*8 + kb%8.
+ *   FP4 scales ([N, K/32]): 32-byte tiles, scale (n, j) at
+ *         ((n/16)*(K/64) + j/2)*32 + (n%16)*2 + j%2.
+ *   Experts follow each other as in the row layout (expert e at e*N*K elements).
+ * Returns MOE_ERR_INVALID_ARG for a NULL cfg/src/dst, a NULL dst member whose
+ * src member is set, or an fp32 layer; validation as moe_validate_config. */
+int moe_pack_weights(const moe_config *cfg, const moe_weights *src,
+                     const moe_weights *dst, void *stream);
 
 /* Workspace needed by moe_forward for T tokens, and where each part lives.
  * Host-only; layout may be NULL.  Returns MOE_OK or a validation error. */

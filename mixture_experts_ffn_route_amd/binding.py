@@ -12,7 +12,9 @@ import os
 import numpy as np
 import torch  # loaded first so the library binds to the same HIP runtime as torch
 
-from .config import DTYPE, ROUTE, SCORE, MoEConfig
+from dataclasses import replace
+
+from .config import DTYPE, LAYOUT, ROUTE, SCORE, MoEConfig
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
@@ -27,6 +29,7 @@ MOE_FLAG_EXPERT_RANGE = 2
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout",
     "moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_profiled",
+    "moe_pack_weights",
 )
 MOE_STAGES = ("route", "permute", "gemm1", "gemm2", "combine")
 
@@ -40,7 +43,7 @@ class MoeConfigC(ctypes.Structure):
         ("route_scale", ctypes.c_float), ("renormalize", ctypes.c_int32),
         ("swiglu_limit", ctypes.c_float), ("route_mode", ctypes.c_int32),
         ("vocab_size", ctypes.c_int64), ("act_dtype", ctypes.c_int32),
-        ("expert_dtype", ctypes.c_int32),
+        ("expert_dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -73,10 +76,11 @@ def _load():
     lib.moe_route.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, vp]
     lib.moe_permute.argtypes = [cfgp, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_forward.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_pack_weights.argtypes = [cfgp, wp, wp, vp]
     lib.moe_forward_profiled.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t,
                                          ctypes.POINTER(ctypes.c_void_p), vp]
     for f in ("moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout", "moe_route",
-              "moe_permute", "moe_forward", "moe_forward_profiled"):
+              "moe_permute", "moe_forward", "moe_forward_profiled", "moe_pack_weights"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -118,7 +122,7 @@ def config_c(cfg: MoEConfig) -> MoeConfigC:
         cfg.dim, cfg.n_routed_experts, cfg.n_activated_experts, cfg.n_expert_groups,
         cfg.n_limited_groups, cfg.moe_inter_dim, cfg.n_shared_experts, SCORE[cfg.score_func],
         cfg.route_scale, cfg.renormalize, cfg.swiglu_limit, ROUTE[cfg.route_mode],
-        cfg.vocab_size, DTYPE[cfg.act_dtype], DTYPE[cfg.expert_dtype])
+        cfg.vocab_size, DTYPE[cfg.act_dtype], DTYPE[cfg.expert_dtype], LAYOUT[cfg.weight_layout])
 
 
 def weights_c(layer: dict) -> MoeWeightsC:
@@ -169,6 +173,27 @@ def moe_permute(cfg: MoEConfig, indices, T: int, counts, offsets, sorted_tok, so
     _check(_lib.moe_permute(ctypes.byref(config_c(cfg)), _ptr(indices), T, _ptr(counts),
                             _ptr(offsets), _ptr(sorted_tok), _ptr(sorted_slot), _ptr(inverse),
                             _ptr(flags), _stream(stream)), "moe_permute")
+
+
+PACKED_MEMBERS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                  "sh_gate", "sh_up", "sh_down")
+
+
+def moe_pack_weights(cfg: MoEConfig, src: dict, dst: dict, stream=None):
+    _check(_lib.moe_pack_weights(ctypes.byref(config_c(cfg)), ctypes.byref(weights_c(src)),
+                                 ctypes.byref(weights_c(dst)), _stream(stream)),
+           "moe_pack_weights")
+
+
+def pack_layer(cfg: MoEConfig, layer: dict, stream=None):
+    """(cfg with weight_layout "tiled", a copy of `layer` whose expert matrices
+    are freshly allocated tiled copies written by moe_pack_weights)."""
+    out = dict(layer)
+    for n in PACKED_MEMBERS:
+        if layer.get(n) is not None:
+            out[n] = torch.empty_like(layer[n])
+    moe_pack_weights(cfg, layer, out, stream)
+    return replace(cfg, weight_layout="tiled"), out
 
 
 def moe_forward(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, ws, stream=None,

@@ -10,6 +10,7 @@ from dataclasses import dataclass, field, replace
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
 ROUTE = {"learned": 0, "hash": 1}
 DTYPE = {"f32": 0, "bf16": 1, "fp4": 2}
+LAYOUT = {"rows": 0, "tiled": 1}
 
 
 @dataclass(frozen=True)
@@ -30,6 +31,7 @@ class MoEConfig:
     act_dtype: str = "bf16"
     expert_dtype: str = "bf16"
     has_bias: bool = False
+    weight_layout: str = "rows"   # expert matrices as given ("rows") or packed ("tiled")
 
     @property
     def renorm(self):

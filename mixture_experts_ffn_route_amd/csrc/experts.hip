@@ -46,6 +46,7 @@ struct GemmArgs {
   int n_slabs;
   float limit;               // SwiGLU clamp (two-matrix form); <= 0: none
   const float *sorted_w;     // one-matrix form: gate value of each permuted row
+  int tiled;                 // B, S, SB in the tiled layout (moe_pack_weights)
   int64_t routed_rows;       // T * k: rows at or above this belong to the shared expert
 };
 
@@ -147,21 +148,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
     asrc[i] = g.A + src * K + koff;
   }
 
-  // ---- weight pointers ----
+  // ---- weight pointers: this lane's operand of stage 0, plus the byte
+  // strides between stages (bst), between the two 32-input halves of a bf16
+  // stage (qst) and between the scale bytes of two FP4 stages (sst).  Row
+  // layout: the operand is 8 (bf16) or 16 (FP4) inputs of row n; tiled layout:
+  // lane `lane` of the tile's contiguous 1 KB / 512 B block. ----
   const uint8_t *bptr[NB][NCB];
   const uint8_t *sptr[NB][NCB];
+  const bool tiled = g.tiled != 0;
+  const int64_t bst = FP4 ? (tiled ? 512 : BK / 2) : (tiled ? SUBS * 1024 : BK * 2);
+  const int64_t qst = tiled ? 1024 : 64;
+  const int64_t sst = tiled ? 32 : BK / 32;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int64_t n = col0 + cb * 16 + r16;
+      const int64_t nb = (col0 + cb * 16) >> 4;    // column block of this 16-wide slice
       if constexpr (FP4) {
         const int64_t K2 = K / 2, K32 = K / 32;
-        bptr[b][cb] = (const uint8_t *)g.B[b] + ((int64_t)t.grp * N + n) * K2 + jq * 8;
-        sptr[b][cb] = g.S[b] + ((int64_t)t.grp * N + n) * K32 + (jq >> 1);
+        const uint8_t *mat = (const uint8_t *)g.B[b] + (int64_t)t.grp * N * K2;
+        const uint8_t *smat = g.S[b] + (int64_t)t.grp * N * K32;
+        if (tiled) {
+          bptr[b][cb] = mat + nb * (K / 64) * 512 + lane * 8;
+          sptr[b][cb] = smat + nb * (K / 64) * 32 + r16 * 2 + (jq >> 1);
+        } else {
+          bptr[b][cb] = mat + n * K2 + jq * 8;
+          sptr[b][cb] = smat + n * K32 + (jq >> 1);
+        }
       } else {
         const bf16 *base = t.shared ? g.SB[b] : (const bf16 *)g.B[b] + (int64_t)t.grp * N * K;
-        bptr[b][cb] = (const uint8_t *)(base + n * K + jq * 8);
+        bptr[b][cb] = tiled ? (const uint8_t *)base + nb * (K / 32) * 1024 + lane * 16
+                            : (const uint8_t *)(base + n * K + jq * 8);
         sptr[b][cb] = nullptr;
       }
     }
@@ -188,12 +206,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
     } else if constexpr (FP4) {
       const int r = q - NFW, bc = r >> 1, b = bc / NCB, cb = bc - b * NCB;
       if ((r & 1) == 0)
-        fq[SL][b][cb] = *(const uint2 *)(bptr[b][cb] + (int64_t)ST * (BK / 2));
+        fq[SL][b][cb] = *(const uint2 *)(bptr[b][cb] + ST * bst);
       else
-        sq[SL][b][cb] = sptr[b][cb][ST * (BK / 32)];
+        sq[SL][b][cb] = sptr[b][cb][ST * sst];
     } else {
       const int r = q - NFW, bc = r / NQ, qq = r - bc * NQ, b = bc / NCB, cb = bc - b * NCB;
-      bq[SL][b][cb][qq] = *(const u32x4 *)(bptr[b][cb] + ((int64_t)ST * BK + qq * 32) * 2);
+      bq[SL][b][cb][qq] = *(const u32x4 *)(bptr[b][cb] + ST * bst + qq * qst);
     }
   };
   auto issue_stage = [&](int SL, int ST) {
@@ -604,6 +622,7 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   a.tile_count = p.tile_count;
   a.routed_rows = routed_rows;
   a.sorted_w = p.sorted_w;
+  a.tiled = p.tiled ? 1 : 0;
 
   // GEMM1: gate|up + SwiGLU -> H
   a.A = (const bf16 *)p.x;

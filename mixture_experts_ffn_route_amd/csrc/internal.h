@@ -43,6 +43,7 @@ struct ExpertPlan {
   bool has_shared;
   float swiglu_limit;
   int act_dtype, expert_dtype;
+  bool tiled;            // expert matrices in MOE_LAYOUT_TILED
   const void *x;
   const moe_weights *w;
   const float *route_w;
@@ -60,5 +61,10 @@ struct ExpertPlan {
 int choose_tile_rows(const moe_config &cfg, int64_t T);
 
 hipError_t launch_experts(const ExpertPlan &p, hipStream_t s);
+
+// Rewrite `count` consecutive [N, K] expert matrices (bf16 or FP4 codes) or
+// their E8M0 scales (scales = true) from the row layout into the tiled one.
+hipError_t launch_pack_matrix(const void *src, void *dst, int64_t count, int64_t N, int64_t K,
+                              int dtype, bool scales, hipStream_t s);
 
 }  // namespace moe

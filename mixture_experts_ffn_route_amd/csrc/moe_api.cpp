@@ -47,6 +47,10 @@ int validate(const moe_config *c) {
   } else {
     return MOE_ERR_INVALID_ARG;
   }
+  if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_TILED)
+    return MOE_ERR_INVALID_ARG;
+  if (c->weight_layout == MOE_LAYOUT_TILED && c->act_dtype != MOE_DTYPE_BF16)
+    return MOE_ERR_UNSUPPORTED;
   if (k > 16 || E > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->route_mode == MOE_ROUTE_HASH) {
     if (c->vocab_size < 1) return MOE_ERR_INVALID_ARG;
@@ -273,6 +277,7 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   p.swiglu_limit = cfg->swiglu_limit;
   p.act_dtype = cfg->act_dtype;
   p.expert_dtype = cfg->expert_dtype;
+  p.tiled = cfg->weight_layout == MOE_LAYOUT_TILED;
   p.x = x;
   p.w = w;
   p.route_w = route_w;
@@ -292,6 +297,39 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   p.y = y;
   p.events = events;
   return hip_status(moe::launch_experts(p, s));
+}
+
+int moe_pack_weights(const moe_config *cfg, const moe_weights *src, const moe_weights *dst,
+                     void *stream) {
+  if (!cfg || !src || !dst) return MOE_ERR_INVALID_ARG;
+  moe_config c = *cfg;
+  c.weight_layout = MOE_LAYOUT_ROWS;
+  const int st = validate(&c);
+  if (st != MOE_OK) return st;
+  if (c.act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  const int64_t E = c.n_routed_experts, d = c.dim, I = c.moe_inter_dim;
+  const int ed = c.expert_dtype;
+  struct Job { const void *s; const void *d; int64_t count, N, K; int dtype; bool scales; };
+  const Job jobs[] = {
+      {src->w_gate, dst->w_gate, E, I, d, ed, false},
+      {src->w_up, dst->w_up, E, I, d, ed, false},
+      {src->w_down, dst->w_down, E, d, I, ed, false},
+      {ed == MOE_DTYPE_FP4_E2M1 ? src->s_gate : nullptr, dst->s_gate, E, I, d, ed, true},
+      {ed == MOE_DTYPE_FP4_E2M1 ? src->s_up : nullptr, dst->s_up, E, I, d, ed, true},
+      {ed == MOE_DTYPE_FP4_E2M1 ? src->s_down : nullptr, dst->s_down, E, d, I, ed, true},
+      {src->sh_gate, dst->sh_gate, 1, I, d, MOE_DTYPE_BF16, false},
+      {src->sh_up, dst->sh_up, 1, I, d, MOE_DTYPE_BF16, false},
+      {src->sh_down, dst->sh_down, 1, d, I, MOE_DTYPE_BF16, false},
+  };
+  for (const Job &j : jobs)
+    if (j.s && (!j.d || j.d == j.s)) return MOE_ERR_INVALID_ARG;
+  for (const Job &j : jobs) {
+    if (!j.s) continue;
+    const hipError_t e = moe::launch_pack_matrix(j.s, const_cast<void *>(j.d), j.count, j.N,
+                                                 j.K, j.dtype, j.scales, (hipStream_t)stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,

@@ -67,6 +67,7 @@ BAD = [
     ("k > 16", replace(V3, n_activated_experts=17, n_limited_groups=8), B.MOE_ERR_UNSUPPORTED),
     ("learned E > 512", replace(V3, n_routed_experts=1024, n_expert_groups=1, n_limited_groups=1), B.MOE_ERR_UNSUPPORTED),
     ("group lanes not a power of two", replace(V3, n_routed_experts=96, n_expert_groups=8, n_limited_groups=4), B.MOE_ERR_UNSUPPORTED),
+    ("tiled fp32 layer", replace(C.TINY_FP32.cfg, weight_layout="tiled"), B.MOE_ERR_UNSUPPORTED),
 ]
 
 
@@ -84,6 +85,32 @@ def test_enum_range_checked():
     c.route_mode = 2
     assert B._lib.moe_validate_config(ctypes.byref(c)) == B.MOE_ERR_INVALID_ARG
     assert B._lib.moe_validate_config(None) == B.MOE_ERR_INVALID_ARG
+    c = B.config_c(V3)
+    c.weight_layout = 2
+    assert B._lib.moe_validate_config(ctypes.byref(c)) == B.MOE_ERR_INVALID_ARG
+    assert B.moe_validate_config(replace(V3, weight_layout="tiled")) == B.MOE_OK
+
+
+def test_pack_rejects_before_any_launch():
+    """moe_pack_weights checks its arguments on the host: null structs, a set
+    source member without a destination, in-place packing, fp32 layers."""
+    fake, other = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000)
+    cc = B.config_c(V3)
+    full = B.MoeWeightsC(*([fake] * 12))
+    pack = B._lib.moe_pack_weights
+    assert pack(None, ctypes.byref(full), ctypes.byref(full), None) == B.MOE_ERR_INVALID_ARG
+    assert pack(ctypes.byref(cc), None, ctypes.byref(full), None) == B.MOE_ERR_INVALID_ARG
+    assert pack(ctypes.byref(cc), ctypes.byref(full), None, None) == B.MOE_ERR_INVALID_ARG
+    assert pack(ctypes.byref(cc), ctypes.byref(full), ctypes.byref(full), None) == B.MOE_ERR_INVALID_ARG
+    dst = B.MoeWeightsC(*([other] * 12))
+    dst.w_up = None
+    assert pack(ctypes.byref(cc), ctypes.byref(full), ctypes.byref(dst), None) == B.MOE_ERR_INVALID_ARG
+    f32 = B.config_c(C.TINY_FP32.cfg)
+    assert pack(ctypes.byref(f32), ctypes.byref(full), ctypes.byref(B.MoeWeightsC(*([other] * 12))),
+                None) == B.MOE_ERR_INVALID_ARG
+    bad = B.config_c(replace(V3, dim=7168 + 32))
+    assert pack(ctypes.byref(bad), ctypes.byref(full), ctypes.byref(B.MoeWeightsC(*([other] * 12))),
+                None) == B.MOE_ERR_UNSUPPORTED
 
 
 def test_forward_rejects_before_any_launch():

@@ -2,6 +2,8 @@
 benchmark times (same entry point, same token count, hence the same tile
 and kernel choices).
 
+bf16 and FP4 layers run on tiled weights (moe_pack_weights), as the
+benchmark does, and must match the row layout bit for bit.
 Routing and the permutation are compared for every token.  The layer output
 is compared on a sample of tokens the float64 oracle computes one by one
 (first, last and seeded random positions; every token for the decode batch
@@ -49,11 +51,23 @@ def test_forward_full_size(name, gpu):
         layer["tid2eid"] = torch.from_numpy(table).to(gpu)
     ws = B.alloc_workspace(cfg, T, gpu)
     y = torch.empty_like(layer["x"])
-    print(f"[full] {name}: forward", flush=True)
-    B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y, ws)
+    if cfg.act_dtype == "bf16":
+        print(f"[full] {name}: packing the expert weights", flush=True)
+        run_cfg, run_layer = B.pack_layer(cfg, layer)
+    else:
+        run_cfg, run_layer = cfg, layer
+    print(f"[full] {name}: forward ({run_cfg.weight_layout} weights)", flush=True)
+    B.moe_forward(run_cfg, run_layer, layer["x"], layer["token_ids"], T, y, ws)
     torch.cuda.synchronize()
     v = B.workspace_views(cfg, T, ws)
     assert int(v["flags"][0]) == 0
+    if run_cfg is not cfg:
+        y_rows = torch.empty_like(y)
+        ws_rows = B.alloc_workspace(cfg, T, gpu)
+        B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y_rows, ws_rows)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_rows.view(torch.int16))
+        del y_rows, ws_rows, run_layer
 
     # routing of every token
     print(f"[full] {name}: oracle routing", flush=True)
