@@ -558,22 +558,22 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
   if (nb == 2) {
     if (fp4) {
       if (decode) { MOE_TRY(4, 2, 2, true, 4) }
-      else { MOE_TRY(4, 2, 2, true, 3) }
+      else { MOE_TRY(8, 2, 1, true, 3) }
       MOE_TRY(4, 2, 1, true, 3)
     } else {
-      if (decode) { MOE_TRY(4, 2, 2, false, 4) }
+      if (decode) { MOE_TRY(4, 2, 1, false, 4) }
+      else if (mb >= 16) { MOE_TRY(8, 2, 1, false, 4) }
       else { MOE_TRY(8, 2, 1, false, 3) }
       MOE_TRY(4, 2, 1, false, 3)
     }
   } else {
     if (fp4) {
       if (decode) { MOE_TRY(4, 1, 4, true, 4) }
-      else { MOE_TRY(4, 1, 4, true, 3) }
+      else { MOE_TRY(8, 1, 2, true, 3) }
       MOE_TRY(4, 1, 1, true, 3)
     } else {
-      if (decode) { MOE_TRY(4, 1, 4, false, 4) }
-      else if (mb >= 16) { MOE_TRY(8, 1, 1, false, 4) }
-      else { MOE_TRY(4, 1, 4, false, 3) }
+      if (decode) { MOE_TRY(4, 1, 2, false, 4) }
+      else { MOE_TRY(8, 1, 2, false, 3) }
       MOE_TRY(4, 1, 1, false, 3)
     }
   }
