@@ -151,34 +151,38 @@ __device__ __forceinline__ void select_token(const RouteArgs &a, const float *zr
 
 // ---------------------------------------------------------------------------
 // bf16 layers: logits on MFMA.  MT 16-token row blocks per workgroup; the E
-// experts are cut into 16-wide column blocks, wave w owning blocks w, w+4, ...
-// (EPL = ceil(E/64) of them, the same count as experts per lane in phase 2).
-template <int EPL, int MT>
-__global__ __launch_bounds__(256) void route_learned_bf16(const RouteArgs a) {
-  constexpr int BT = 16 * MT;
+// experts are cut into 16-wide column blocks, wave group member c (of 4)
+// owning blocks c, c+4, ... (EPL = ceil(E/64) of them, the same count as
+// experts per lane in phase 2).  KS wave groups split the input dimension;
+// their partial logits are added in LDS in a fixed order.  Each wave keeps
+// NSR k-steps of operands in flight in a register ring; every load is
+// unconditional (rows past T or E re-read a valid row and their logits are
+// dropped), so the compiler's waits stay static.
+template <int EPL, int MT, int KS>
+__global__ __launch_bounds__(256 * KS) void route_learned_bf16(const RouteArgs a) {
+  constexpr int BT = 16 * MT, NSR = 4;
   extern __shared__ float zl[];                 // [BT][E + 1]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wc = wave & 3, ks = wave >> 2;
   const int64_t t0 = (int64_t)blockIdx.x * BT;
   const int E = a.E, d = a.d, ldz = E + 1;
+  const int dk = d / KS;                        // d % 64 == 0, so dk % 32 == 0
+  const int nsteps = dk / 32;
   const bf16 *x = (const bf16 *)a.x;
   const bf16 *w = (const bf16 *)a.w;
 
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   const bf16 *xrow[MT];
-  bool xok[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int64_t t = t0 + m * 16 + r16;
-    xok[m] = t < a.T;
-    xrow[m] = x + (xok[m] ? t : 0) * (int64_t)d + kq;
+    xrow[m] = x + (t < a.T ? t : a.T - 1) * (int64_t)d + ks * dk + kq;
   }
   const bf16 *wrow[EPL];
-  bool wok[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
-    const int e = (wave + 4 * j) * 16 + r16;
-    wok[j] = e < E;
-    wrow[j] = w + (int64_t)(wok[j] ? e : 0) * d + kq;
+    const int e = (wc + 4 * j) * 16 + r16;
+    wrow[j] = w + (int64_t)(e < E ? e : E - 1) * d + ks * dk + kq;
   }
   f32x4 acc[MT][EPL];
 #pragma unroll
@@ -186,43 +190,55 @@ __global__ __launch_bounds__(256) void route_learned_bf16(const RouteArgs a) {
 #pragma unroll
     for (int j = 0; j < EPL; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bf16x8 zero8 = {};
-  bf16x8 an[MT], bn[EPL];
+  bf16x8 an[NSR][MT], bn[NSR][EPL];
+  auto load = [&](int slot, int step) {
+    const int off = step * 32;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) an[m] = xok[m] ? *(const bf16x8 *)(xrow[m]) : zero8;
+    for (int m = 0; m < MT; ++m) an[slot][m] = *(const bf16x8 *)(xrow[m] + off);
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) bn[j] = wok[j] ? *(const bf16x8 *)(wrow[j]) : zero8;
-  for (int kk = 0; kk < d; kk += 32) {
-    bf16x8 ac[MT], bc[EPL];
+    for (int j = 0; j < EPL; ++j) bn[slot][j] = *(const bf16x8 *)(wrow[j] + off);
+  };
+  const int last = nsteps - 1;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) ac[m] = an[m];
+  for (int p = 0; p < NSR - 1; ++p) load(p, p < last ? p : last);
+  for (int s0 = 0; s0 < nsteps; s0 += NSR) {
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) bc[j] = bn[j];
-    if (kk + 32 < d) {
+    for (int p = 0; p < NSR; ++p) {
+      const int st = s0 + p;
+      const int nx = st + NSR - 1;
+      load((p + NSR - 1) % NSR, nx < last ? nx : last);
+      if (st < nsteps) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m) an[m] = xok[m] ? *(const bf16x8 *)(xrow[m] + kk + 32) : zero8;
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) bn[j] = wok[j] ? *(const bf16x8 *)(wrow[j] + kk + 32) : zero8;
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int j = 0; j < EPL; ++j)
-        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac[m], bc[j], acc[m][j], 0, 0, 0);
-  }
-  // logits -> LDS: lane holds expert column r16 of each block, rows 4*(lane>>4)+i
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const int e = (wave + 4 * j) * 16 + r16;
-      if (e < E) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zl[(m * 16 + (lane >> 4) * 4 + i) * ldz + e] = acc[m][j][i];
+          for (int j = 0; j < EPL; ++j)
+            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(an[p][m], bn[p][j], acc[m][j],
+                                                                0, 0, 0);
       }
     }
-  __syncthreads();
-  for (int tl = wave; tl < BT; tl += 4) {
+  }
+  // logits -> LDS: lane holds expert column r16 of each block, rows
+  // 4*(lane>>4)+i; the K parts are summed in order ks = 0, 1, ...
+#pragma unroll
+  for (int part = 0; part < KS; ++part) {
+    if (ks == part) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = (wc + 4 * j) * 16 + r16;
+          if (e < E) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float *z = zl + (m * 16 + (lane >> 4) * 4 + i) * ldz + e;
+              *z = part == 0 ? acc[m][j][i] : *z + acc[m][j][i];
+            }
+          }
+        }
+    }
+    __syncthreads();
+  }
+  for (int tl = wave; tl < BT; tl += 4 * KS) {
     const int64_t t = t0 + tl;
     if (t < a.T) select_token<EPL>(a, zl + tl * ldz, t, lane);
   }
@@ -275,14 +291,20 @@ __global__ __launch_bounds__(256) void route_hash(const int32_t *token_ids, cons
 template <int EPL>
 static hipError_t launch_learned_epl(const RouteArgs &a, int act_dtype, hipStream_t s) {
   if (act_dtype == MOE_DTYPE_BF16) {
-    const int MT = a.T >= 2048 ? 2 : 1;
+    // one 16-token block per workgroup until that gives more workgroups than
+    // CUs, then two (halves the gate-weight re-reads from L2)
+    const int MT = a.T > 4096 ? 2 : 1;
     const int BT = 16 * MT;
     const size_t lds = (size_t)BT * (a.E + 1) * sizeof(float);
     const dim3 grid((unsigned)((a.T + BT - 1) / BT));
-    if (MT == 2)
-      hipLaunchKernelGGL((route_learned_bf16<EPL, 2>), grid, dim3(256), lds, s, a);
-    else
-      hipLaunchKernelGGL((route_learned_bf16<EPL, 1>), grid, dim3(256), lds, s, a);
+    if (MT == 2) {
+      if (lds > 65536)
+        (void)hipFuncSetAttribute((const void *)route_learned_bf16<EPL, 2, 2>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipLaunchKernelGGL((route_learned_bf16<EPL, 2, 2>), grid, dim3(512), lds, s, a);
+    } else {
+      hipLaunchKernelGGL((route_learned_bf16<EPL, 1, 2>), grid, dim3(512), lds, s, a);
+    }
   } else {
     const size_t lds = (size_t)16 * (a.E + 1) * sizeof(float);
     const dim3 grid((unsigned)((a.T + 15) / 16));
