@@ -130,22 +130,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
       }
   }
 
-  // ---- this wave's A fragments f = wave + WAVES*i (copies past NFRAG
-  // re-read fragment 0 into slots nobody reads, so every wave issues NFW) ----
+  // ---- activation copies.  A stage holds, per 16-row block m, two 1 KB
+  // copy units h = 0, 1 of 8 rows x 64 inputs (each row one full 128-byte
+  // line).  Lane l of unit (m, h) fetches row 16m + 8h + l/8, 8-input chunk
+  // (l%8) ^ (l/8), which lands at byte 16*l of the unit; this wave's units
+  // are f = wave + WAVES*i (units past NFRAG re-read unit 0 into slots nobody
+  // reads, so every wave issues NFW). ----
+  static_assert(SUBS == 2, "two copy units per row block and stage");
   const bf16 *asrc[NFW];
 #pragma unroll
   for (int i = 0; i < NFW; ++i) {
     const int f0 = wave + WAVES * i;
     const int f = f0 < NFRAG ? f0 : 0;
-    const int m = f / SUBS, s = f - m * SUBS;
-    int r = m * 16 + r16;
+    const int m = f >> 1, h = f & 1;
+    int r = m * 16 + 8 * h + (lane >> 3);
     r = r < rows ? r : rows - 1;
     const int64_t src = g.a_rows ? g.a_rows[row0 + r] : (int64_t)(row0 + r);
-    // bf16 keeps k = 32s + 8jq; FP4 uses k = 16jq + 8s so that each lane's 16
-    // weight codes of a stage lie in one 32-input scale block.  A and B use
-    // the same order, so the products are unchanged.
-    const int koff = FP4 ? (16 * jq + 8 * s) : (32 * s + 8 * jq);
-    asrc[i] = g.A + src * K + koff;
+    asrc[i] = g.A + src * K + 8 * ((lane & 7) ^ (lane >> 3));
+  }
+  // MFMA operand of k-step `sub`: row r16, 8-input chunk c of the stage.
+  // bf16 keeps k = 32 sub + 8 jq (c = 4 sub + jq); FP4 uses k = 16 jq + 8 sub
+  // (c = 2 jq + sub) so that each lane's 16 weight codes of a stage lie in one
+  // 32-input scale block.  A and B use the same order, so the products are
+  // unchanged.  Within every 8-lane group the chunk ^ row values differ, so
+  // the 16-byte reads hit distinct LDS banks.
+  int aoff[SUBS];
+#pragma unroll
+  for (int sub = 0; sub < SUBS; ++sub) {
+    const int c = FP4 ? (2 * jq + sub) : (4 * sub + jq);
+    const int rr = r16 & 7;
+    aoff[sub] = (r16 >> 3) * FRAG + (rr * 8 + (c ^ rr)) * 8;
   }
 
   // ---- weight pointers: this lane's operand of stage 0, plus the byte
@@ -242,7 +256,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
       const int nx = st + NS - 1 < last ? st + NS - 1 : last;
       if (st >= nst) issue_stage(nslot, nx);
       if (st < nst) {
-        const bf16 *abase = As + p * SLOT + lane * 8;
+        const bf16 *abase = As + p * SLOT;
 #pragma unroll
         for (int sub = 0; sub < SUBS; ++sub) {
           bf16x8 bf[NB][NCB];
@@ -267,7 +281,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
             bf16x8 a[CH];
 #pragma unroll
             for (int j = 0; j < CH; ++j)
-              a[j] = *(const bf16x8 *)(abase + ((mc + j) * SUBS + sub) * FRAG);
+              a[j] = *(const bf16x8 *)(abase + aoff[sub] + (mc + j) * 2 * FRAG);
 #pragma unroll
             for (int j = 0; j < CH; ++j)
 #pragma unroll
