@@ -136,6 +136,9 @@ typedef struct {
   size_t tiles;                /* int32 [max_tiles, 4] GEMM work list           */
   size_t tile_count;           /* int32 [1]      tiles written by the permute    */
   size_t flags;                /* uint32 [4]     device error flags (below)      */
+  size_t route_logits;         /* float          partial gate logits (learned
+                                  bf16 routing; 0 bytes otherwise)               */
+  size_t perm_hist;            /* int32          per-chunk expert histograms     */
   size_t h;                    /* [T*k + T, I]   SwiGLU activations (bf16/f32)   */
   size_t yrows;                /* [T*k + T, dim] weighted expert outputs         */
   int32_t max_tiles;

@@ -56,7 +56,8 @@ class MoeWeightsC(ctypes.Structure):
 class MoeWsLayoutC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total_bytes", "route_weights", "route_indices", "counts", "offsets", "sorted_tok",
-        "sorted_slot", "sorted_weight", "inverse", "tiles", "tile_count", "flags", "h", "yrows")] + [
+        "sorted_slot", "sorted_weight", "inverse", "tiles", "tile_count", "flags",
+        "route_logits", "perm_hist", "h", "yrows")] + [
         ("max_tiles", ctypes.c_int32), ("tile_rows", ctypes.c_int32)]
 
 
@@ -276,6 +277,7 @@ def workspace_views(cfg: MoEConfig, T: int, ws):
         "tiles": view(lay["tiles"], 4 * lay["max_tiles"], torch.int32).view(-1, 4),
         "tile_count": view(lay["tile_count"], 1, torch.int32),
         "flags": view(lay["flags"], 4, torch.int32),
+        "perm_hist": view(lay["perm_hist"], -(-T * k // 256) * E, torch.int32),
         "h": view(lay["h"], rows * cfg.moe_inter_dim, edt).view(rows, cfg.moe_inter_dim),
         "yrows": view(lay["yrows"], rows * cfg.dim, edt).view(rows, cfg.dim),
         "layout": lay,

@@ -47,6 +47,9 @@ struct GemmArgs {
   float limit;               // SwiGLU clamp (two-matrix form); <= 0: none
   const float *sorted_w;     // one-matrix form: gate value of each permuted row
   int tiled;                 // B, S, SB in the tiled layout (moe_pack_weights)
+  float *Cf;                 // one-matrix form: fp32 output instead of C, or null
+  int64_t dense_rows;        // tiles == null: one group of this many rows, cut
+  int dense_tile_rows;       //   into tiles of dense_tile_rows rows
   int64_t routed_rows;       // T * k: rows at or above this belong to the shared expert
 };
 
@@ -334,9 +337,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + jq * 4 + i;
         if (row < rows) {
-          bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
+          const int64_t o = (int64_t)(row0 + row) * N + col0 + r16;
+          if (g.Cf) {
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) crow[cb * 16] = (bf16)(acc[m][0][cb][i] * row_w[m][i]);
+            for (int cb = 0; cb < NCB; ++cb) g.Cf[o + cb * 16] = acc[m][0][cb][i] * row_w[m][i];
+          } else {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) g.C[o + cb * 16] = (bf16)(acc[m][0][cb][i] * row_w[m][i]);
+          }
         }
       }
   }
@@ -378,9 +386,16 @@ void grouped_gemm(const GemmArgs g) {
   const int slab = (int)(item - (int64_t)(tile - g.tile_begin) * g.n_slabs);
 
   TileCtx t;
-  t.grp = g.tiles[4 * tile];
-  t.row0 = g.tiles[4 * tile + 1];
-  t.rows = g.tiles[4 * tile + 2];
+  if (g.tiles) {
+    t.grp = g.tiles[4 * tile];
+    t.row0 = g.tiles[4 * tile + 1];
+    t.rows = g.tiles[4 * tile + 2];
+  } else {
+    t.grp = 0;
+    t.row0 = tile * g.dense_tile_rows;
+    const int64_t left = g.dense_rows - t.row0;
+    t.rows = left < g.dense_tile_rows ? (int)left : g.dense_tile_rows;
+  }
   t.shared = t.grp == g.E;
   t.K = g.K;
   t.N = g.N;
@@ -593,6 +608,24 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
   }
 #undef MOE_TRY
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_dense_logits(const void *x, const void *w, int64_t T, int d, int E, float *z,
+                               hipStream_t s) {
+  if (E % 64 != 0 || d % 64 != 0) return hipErrorInvalidValue;
+  GemmArgs a = {};
+  a.A = (const bf16 *)x;
+  a.K = d;
+  a.N = E;
+  a.B[0] = w;
+  a.E = 1;                                   // group 0 is never the shared group
+  a.Cf = z;
+  a.dense_rows = T;
+  a.dense_tile_rows = 64;
+  a.tile_begin = 0;
+  a.tile_end = (int)((T + 63) / 64);
+  a.n_slabs = E / 64;
+  return run_gemm<4, 1, 1, 4, false, 3>(a, a.tile_end, s);
 }
 
 static hipError_t mark(const ExpertPlan &p, int i, hipStream_t s) {

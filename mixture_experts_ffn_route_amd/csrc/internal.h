@@ -8,10 +8,18 @@
 
 namespace moe {
 
-// Learned routing: fused score GEMM + affinity + bias + group limit + top-k.
+// Learned routing: score GEMM + affinity + bias + group limit + top-k.  With
+// `logits` (route_logits_floats(cfg, T) floats of workspace) bf16 layers use
+// the split router; without, one fused kernel keeps the logits in LDS.
 hipError_t launch_route_learned(const moe_config &cfg, const void *x, const void *gate_w,
                                 const float *bias, int64_t T, float *weights,
-                                int32_t *indices, hipStream_t s);
+                                int32_t *indices, hipStream_t s, float *logits = nullptr);
+size_t route_logits_floats(const moe_config &cfg, int64_t T);
+
+// z[T, E] = x[T, d] . w[E, d]^T in fp32 on the grouped-GEMM kernel (one group,
+// 64-row tiles, 64-expert slabs); bf16 operands, E % 64 == 0, d % 64 == 0.
+hipError_t launch_dense_logits(const void *x, const void *w, int64_t T, int d, int E, float *z,
+                               hipStream_t s);
 
 // Hash routing: indices = tid2eid[token_id], weights = route_scale / k.
 hipError_t launch_route_hash(const moe_config &cfg, const int32_t *token_ids,
@@ -29,10 +37,15 @@ struct TileSpec {
   float *sorted_w;           // [T*k]  gate value of each permuted row, or null
 };
 
+// chunk_hist: null (one workgroup) or int32 [permute_chunks(T*k) * E] of
+// workspace, which lets large batches use the many-workgroup kernels.
 hipError_t launch_permute(int E, int k, int64_t T, const int32_t *indices, int32_t *counts,
                           int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,
                           int32_t *inverse, uint32_t *flags, const TileSpec *tiles,
-                          bool clear_flags, hipStream_t s);
+                          bool clear_flags, hipStream_t s, int32_t *chunk_hist = nullptr);
+
+// Chunks of the many-workgroup permutation for `pairs` (token, slot) pairs.
+int64_t permute_chunks(int64_t pairs);
 
 hipError_t launch_clear_flags(uint32_t *flags, hipStream_t s);
 

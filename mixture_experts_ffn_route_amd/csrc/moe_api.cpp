@@ -96,6 +96,8 @@ int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
   l.tiles = take(sizeof(int32_t) * 4 * max_tiles);
   l.tile_count = take(sizeof(int32_t));
   l.flags = take(sizeof(uint32_t) * 4);
+  l.route_logits = take(sizeof(float) * moe::route_logits_floats(*c, T));
+  l.perm_hist = take(sizeof(int32_t) * moe::permute_chunks(T * k) * E);
   l.h = take(es * rows * c->moe_inter_dim);
   l.yrows = take(es * rows * c->dim);
   l.total_bytes = off;
@@ -241,6 +243,8 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   int32_t *tiles = (int32_t *)(base + L.tiles);
   int32_t *tile_count = (int32_t *)(base + L.tile_count);
   uint32_t *flags = (uint32_t *)(base + L.flags);
+  float *logits = (float *)(base + L.route_logits);
+  int32_t *perm_hist = (int32_t *)(base + L.perm_hist);
   const int k = cfg->n_activated_experts;
   const bool hash = cfg->route_mode == MOE_ROUTE_HASH;
 
@@ -250,7 +254,8 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
     if ((e = moe::launch_clear_flags(flags, s)) != hipSuccess) return MOE_ERR_HIP;
     e = moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, route_w, route_idx, flags, s);
   } else {
-    e = moe::launch_route_learned(*cfg, x, w->gate_w, w->gate_bias, T, route_w, route_idx, s);
+    e = moe::launch_route_learned(*cfg, x, w->gate_w, w->gate_bias, T, route_w, route_idx, s,
+                                  moe::route_logits_floats(*cfg, T) ? logits : nullptr);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
 
@@ -264,7 +269,7 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   ts.sorted_w = sorted_w;
   if (events && hipEventRecord(events[MOE_STAGE_PERMUTE], s) != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_permute(cfg->n_routed_experts, k, T, route_idx, counts, offsets, sorted_tok,
-                          sorted_slot, inverse, flags, &ts, /*clear_flags=*/!hash, s);
+                          sorted_slot, inverse, flags, &ts, /*clear_flags=*/!hash, s, perm_hist);
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   moe::ExpertPlan p;

@@ -32,16 +32,22 @@ struct RouteArgs {
 
 // ---------------------------------------------------------------------------
 // Phase 2: selection for one token held by one wavefront.
-// zrow: the token's E logits in LDS.  EPL experts per lane.
+// zrow: the token's E logits (LDS or global), given as `nparts` partial sums
+// `pstride` floats apart that are added in order.  EPL experts per lane.
 template <int EPL>
 __device__ __forceinline__ void select_token(const RouteArgs &a, const float *zrow, int64_t t,
-                                             int lane) {
+                                             int lane, int nparts = 1, int64_t pstride = 0) {
   float s[EPL], key[EPL];
   const int E = a.E;
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane * EPL + j;
-    s[j] = (e < E) ? zrow[e] : -INFINITY;
+    float z = -INFINITY;
+    if (e < E) {
+      z = zrow[e];
+      for (int q = 1; q < nparts; ++q) z += zrow[q * pstride + e];
+    }
+    s[j] = z;
   }
   // affinity
   if (a.score_func == MOE_SCORE_SOFTMAX) {
@@ -244,6 +250,102 @@ __global__ __launch_bounds__(256 * KS) void route_learned_bf16(const RouteArgs a
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split router (moe_forward, which has a workspace for the logits).  The score
+// GEMM is tiled over (16*MT tokens) x (64 experts) x (one of KS parts of the
+// input dimension) so that even a decode batch spreads over many CUs; each of
+// the 4 waves owns 16 experts and keeps NSR k-steps of operands in flight.
+// Partial logits go to zpart[ks][t][e]; route_select_kernel adds the parts in
+// order ks = 0, 1, ... and runs the same selection as the fused kernel.
+template <int MT>
+__global__ __launch_bounds__(256) void route_logits_bf16(const RouteArgs a, float *zpart, int KS) {
+  constexpr int NSR = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * (16 * MT);
+  const int ks = blockIdx.z;
+  const int E = a.E, d = a.d;
+  const int dk = d / KS;                        // a multiple of 32 (host picks KS)
+  const int nsteps = dk / 32;
+  const bf16 *x = (const bf16 *)a.x;
+  const bf16 *w = (const bf16 *)a.w;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int ecol = (blockIdx.y * 4 + wave) * 16;   // first expert of this wave
+  const bf16 *xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t t = t0 + m * 16 + r16;
+    xrow[m] = x + (t < a.T ? t : a.T - 1) * (int64_t)d + ks * dk + kq;
+  }
+  const int ew = ecol + r16;
+  const bf16 *wrow = w + (int64_t)(ew < E ? ew : E - 1) * d + ks * dk + kq;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 an[NSR][MT], bn[NSR];
+  auto load = [&](int slot, int step) {
+    const int off = step * 32;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) an[slot][m] = *(const bf16x8 *)(xrow[m] + off);
+    bn[slot] = *(const bf16x8 *)(wrow + off);
+  };
+  const int last = nsteps - 1;
+#pragma unroll
+  for (int p = 0; p < NSR - 1; ++p) load(p, p < last ? p : last);
+  for (int s0 = 0; s0 < nsteps; s0 += NSR) {
+#pragma unroll
+    for (int p = 0; p < NSR; ++p) {
+      const int st = s0 + p;
+      const int nx = st + NSR - 1;
+      load((p + NSR - 1) % NSR, nx < last ? nx : last);
+      if (st < nsteps) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(an[p][m], bn[p], acc[m], 0, 0, 0);
+      }
+    }
+  }
+  if (ecol >= E) return;
+  const int e = ecol + r16;
+  float *zp = zpart + (int64_t)ks * a.T * E;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + m * 16 + (lane >> 4) * 4 + i;
+      if (t < a.T && e < E) zp[t * E + e] = acc[m][i];
+    }
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, const float *zpart,
+                                                           int KS) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < a.T) select_token<EPL>(a, zpart + t * a.E, t, lane, KS, a.T * (int64_t)a.E);
+}
+
+// Large batches with E % 64 == 0 compute the logits on the grouped-GEMM
+// kernel (activation rows copied to LDS as whole lines and shared by the four
+// waves); small ones use route_logits_bf16 split over the input dimension.
+static bool use_dense_logits(int64_t T, int E) { return T >= 1024 && E % 64 == 0; }
+
+// Split-router shape for T tokens: row blocks per workgroup and input parts.
+static void split_shape(int64_t T, int E, int d, int *mt, int *ks) {
+  *mt = T >= 1024 ? 4 : 1;
+  const int64_t blocks = ((T + 16 * *mt - 1) / (16 * *mt)) * ((E + 63) / 64);
+  int k = 1;
+  while (k < 8 && blocks * k * 2 <= 512 && d % (32 * k * 2) == 0) k *= 2;
+  *ks = k;
+}
+
+size_t route_logits_floats(const moe_config &cfg, int64_t T) {
+  if (cfg.route_mode != MOE_ROUTE_LEARNED || cfg.act_dtype != MOE_DTYPE_BF16) return 0;
+  if (use_dense_logits(T, cfg.n_routed_experts)) return (size_t)T * cfg.n_routed_experts;
+  int mt, ks;
+  split_shape(T, cfg.n_routed_experts, cfg.dim, &mt, &ks);
+  return (size_t)ks * T * cfg.n_routed_experts;
+}
+
 // fp32 layers: logits by FMA (small layers; correctness path).
 template <int EPL>
 __global__ __launch_bounds__(256) void route_learned_f32(const RouteArgs a) {
@@ -313,9 +415,31 @@ static hipError_t launch_learned_epl(const RouteArgs &a, int act_dtype, hipStrea
   return hipGetLastError();
 }
 
+template <int EPL>
+static hipError_t launch_split_epl(const RouteArgs &a, float *zpart, hipStream_t s) {
+  if (use_dense_logits(a.T, a.E)) {
+    const hipError_t e = launch_dense_logits(a.x, a.w, a.T, a.d, a.E, zpart, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(route_select_kernel<EPL>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0,
+                       s, a, (const float *)zpart, 1);
+    return hipGetLastError();
+  }
+  int mt, ks;
+  split_shape(a.T, a.E, a.d, &mt, &ks);
+  const dim3 grid((unsigned)((a.T + 16 * mt - 1) / (16 * mt)), (unsigned)((a.E + 63) / 64),
+                  (unsigned)ks);
+  if (mt == 4)
+    hipLaunchKernelGGL(route_logits_bf16<4>, grid, dim3(256), 0, s, a, zpart, ks);
+  else
+    hipLaunchKernelGGL(route_logits_bf16<1>, grid, dim3(256), 0, s, a, zpart, ks);
+  hipLaunchKernelGGL(route_select_kernel<EPL>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s,
+                     a, (const float *)zpart, ks);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_learned(const moe_config &cfg, const void *x, const void *gate_w,
                                 const float *bias, int64_t T, float *weights,
-                                int32_t *indices, hipStream_t s) {
+                                int32_t *indices, hipStream_t s, float *logits) {
   if (T == 0) return hipSuccess;
   RouteArgs a;
   a.x = x; a.w = gate_w; a.bias = bias; a.T = T;
@@ -326,6 +450,19 @@ hipError_t launch_route_learned(const moe_config &cfg, const void *x, const void
   a.route_scale = cfg.route_scale;
   a.weights = weights; a.indices = indices;
   const int epl = (a.E + 63) / 64;
+  if (logits && cfg.act_dtype == MOE_DTYPE_BF16) {
+    switch (epl) {
+      case 1: return launch_split_epl<1>(a, logits, s);
+      case 2: return launch_split_epl<2>(a, logits, s);
+      case 3: return launch_split_epl<3>(a, logits, s);
+      case 4: return launch_split_epl<4>(a, logits, s);
+      case 5: return launch_split_epl<5>(a, logits, s);
+      case 6: return launch_split_epl<6>(a, logits, s);
+      case 7: return launch_split_epl<7>(a, logits, s);
+      case 8: return launch_split_epl<8>(a, logits, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (epl) {
     case 1: return launch_learned_epl<1>(a, cfg.act_dtype, s);
     case 2: return launch_learned_epl<2>(a, cfg.act_dtype, s);

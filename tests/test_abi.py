@@ -156,7 +156,11 @@ def test_workspace_layout_is_aligned_and_disjoint():
                  "offsets": 4 * (E + 1), "sorted_tok": 4 * (T * k + T), "sorted_slot": 4 * T * k,
                  "sorted_weight": 4 * T * k,
                  "inverse": 4 * T * k, "tiles": 16 * lay["max_tiles"], "tile_count": 4, "flags": 16,
-                 "h": es * rows * cfg.moe_inter_dim, "yrows": es * rows * cfg.dim}
+                 "h": es * rows * cfg.moe_inter_dim, "yrows": es * rows * cfg.dim,
+                 # at least one partial-logit plane for the split bf16 router
+                 "route_logits": 4 * T * E if (cfg.route_mode == "learned"
+                                               and cfg.act_dtype == "bf16") else 0,
+                 "perm_hist": 4 * (-(-T * k // 256)) * E}
         spans = sorted((lay[n], lay[n] + s) for n, s in sizes.items())
         for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
             assert a1 <= b0
