@@ -121,6 +121,15 @@ SMALL_WORKLOADS = {
         MoEConfig(dim=256, n_routed_experts=64, n_activated_experts=6, moe_inter_dim=192,
                   n_expert_groups=4, n_limited_groups=2, score_func="softmax"),
         T=150),
+    "dense_router_ragged": Workload(
+        "dense_router_ragged",
+        replace(V3_PREFILL.cfg, dim=512, moe_inter_dim=128, n_routed_experts=64),
+        T=1100, description="1024+ tokens: GEMM-kernel router (last tile 12 rows), chunked permute"),
+    "split_router_e48": Workload(
+        "split_router_e48",
+        MoEConfig(dim=256, n_routed_experts=48, n_activated_experts=6, moe_inter_dim=128,
+                  score_func="sigmoid", route_scale=1.0, has_bias=True),
+        T=1030, description="1024+ tokens with E % 64 != 0: split router, chunked permute"),
     "sigmoid_noshared_big_tiles": Workload(
         "sigmoid_noshared_big_tiles",
         MoEConfig(dim=320, n_routed_experts=8, n_activated_experts=2, moe_inter_dim=128,
