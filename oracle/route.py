@@ -31,6 +31,15 @@ Hash gate ("How was DeepSeek V4's tid2eid derived?", background section, and
 Ch.11.1 of the FFN history): indices = tid2eid[token_id]; every selected
 expert gets weight route_scale / k (uniform 1/k at route_scale = 1).
 
+2-gram hash gate ("How was DeepSeek V4's tid2eid derived?", section "An
+extreme case"): expert j of the pair (previous id a, current id b) is
+(a * q_j + b) mod n, q_j the j-th smallest prime above the vocabulary size.
+Readings: no preceding token -> a = m; duplicates kept; weights
+route_scale / k.  Pins: tests/test_oracle_ngram.py (hand-worked pairs in
+tests/golden/ngram_small.json, the primes checked by an independent
+Miller-Rabin test and gap scan, the a = 0 closed form, near-uniform loads on
+random pairs).
+
 Pins: tests/test_oracle_route.py (distinct ids, masked groups never win,
 weight sums, full-sort agreement, monotone-affinity reduction to argsort of
 the raw logits, g = G reduction, softmax closed form, bias-invariance of the
@@ -150,4 +159,36 @@ def hash_gate(token_ids, tid2eid, route_scale=1.0):
     k = table.shape[1]
     indices = table[token_ids].astype(np.int64)
     weights = np.full(indices.shape, route_scale / k, dtype=np.float64)
+    return weights, indices
+
+
+def smallest_primes_above(m, k):
+    """The k smallest primes larger than m, by trial division."""
+    out = []
+    q = m + 1
+    while len(out) < k:
+        if q >= 2 and all(q % d for d in range(2, int(q ** 0.5) + 1)):
+            out.append(q)
+        q += 1
+    return out
+
+
+def ngram_hash_gate(prev_ids, token_ids, vocab_size, n_experts, k, route_scale=1.0):
+    """2-gram hash routing ("How was DeepSeek V4's tid2eid derived?", section
+    "An extreme case"): for the pair (a, b) of the preceding and the current
+    token id, expert j is (a * q_j + b) mod n with q_j the j-th smallest prime
+    larger than the vocabulary size m.  Reading: a token with no preceding
+    token (prev id < 0) uses a = m; duplicate experts are kept, as the page
+    allows; the weights are route_scale / k as for the table-based hash."""
+    prev_ids = np.asarray(prev_ids, dtype=np.int64)
+    token_ids = np.asarray(token_ids, dtype=np.int64)
+    primes = smallest_primes_above(vocab_size, k)
+    T = token_ids.shape[0]
+    indices = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        a = int(prev_ids[t]) if prev_ids[t] >= 0 else vocab_size
+        b = int(token_ids[t])
+        for j in range(k):
+            indices[t, j] = (a * primes[j] + b) % n_experts
+    weights = np.full((T, k), route_scale / k, dtype=np.float64)
     return weights, indices

@@ -39,9 +39,18 @@ def tid2eid_greedy(p, n, k):
     """Greedy least-loaded table. Returns (table [m,k] int32, f [n], max_vio, min_vio)."""
     p = np.asarray(p, dtype=np.float64)
     m = p.shape[0]
+    token_order = np.lexsort((np.arange(m), -p))   # p descending, id ascending
+    return tid2eid_greedy_order(p, n, k, token_order)
+
+
+def tid2eid_greedy_order(p, n, k, token_order):
+    """The greedy rule with tokens taken in `token_order` (a permutation of
+    0..m-1) instead of by decreasing frequency -- the randomised variant of
+    the "Reference implementation" section.  Same tie rules."""
+    p = np.asarray(p, dtype=np.float64)
+    m = p.shape[0]
     if not (0 < k <= n):
         raise ValueError("need 0 < k <= n")
-    token_order = np.lexsort((np.arange(m), -p))   # p descending, id ascending
     f = np.zeros(n, dtype=np.float64)
     table = np.zeros((m, k), dtype=np.int32)
     expert_ids = np.arange(n)
@@ -83,3 +92,16 @@ def tid2eid_bruteforce(p, n, k):
             best = obj
             best_table = np.array([combos[c] for c in choice], dtype=np.int32)
     return best, best_table
+
+
+def tid2eid_multistart(p, n, k, orders):
+    """Run the greedy once per token order in `orders` [S, m] and keep the
+    table with the smallest max_vio (the page's "run it multiple times and
+    pick ... the lowest max_vio"); equal max_vio keeps the earlier start.
+    Returns (table, f, max_vio, min_vio, best_start)."""
+    best = None
+    for s_idx, order in enumerate(orders):
+        table, f, mx, mn = tid2eid_greedy_order(p, n, k, np.asarray(order))
+        if best is None or mx < best[2]:
+            best = (table, f, mx, mn, s_idx)
+    return best

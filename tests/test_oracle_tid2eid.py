@@ -88,3 +88,45 @@ def test_rows_distinct_and_mass_conserved():
     assert all(len(set(r)) == 5 for r in table.tolist())
     assert f.sum() == pytest.approx(1.0, rel=1e-12)
     assert mx == pytest.approx(f.max() * 32 - 1) and mn == pytest.approx(f.min() * 32 - 1)
+
+
+# --- randomised multi-start variant ("Reference implementation": process the
+# tokens in a random order, run several times, keep the lowest max_vio) ---
+
+def test_frequency_order_reproduces_the_greedy():
+    rng = np.random.default_rng(11)
+    p = np.sort(rng.dirichlet(np.ones(300)))[::-1]
+    t1, f1, mx1, mn1 = oracle.tid2eid_greedy(p, 16, 4)
+    order = np.lexsort((np.arange(300), -p))
+    t2, f2, mx2, mn2 = oracle.tid2eid_greedy_order(p, 16, 4, order)
+    np.testing.assert_array_equal(t1, t2)
+    assert (mx1, mn1) == (mx2, mn2)
+
+
+def test_multistart_hand_worked():
+    # m = 3, n = 2, k = 1, p = (.5, .3, .2)
+    # order (0,1,2): e0 <- .5, e1 <- .3, e1 <- .2 -> loads (.5, .5), max_vio 0
+    # order (2,1,0): e0 <- .2, e1 <- .3, e0 <- .5 -> loads (.7, .3), max_vio .4
+    p = np.array([0.5, 0.3, 0.2])
+    table, f, mx, mn, best = oracle.tid2eid_multistart(p, 2, 1, [[2, 1, 0], [0, 1, 2]])
+    assert best == 1
+    assert table[:, 0].tolist() == [0, 1, 1]
+    assert mx == pytest.approx(0.0, abs=1e-15) and mn == pytest.approx(0.0, abs=1e-15)
+    t_bad, _, mx_bad, _ = oracle.tid2eid_greedy_order(p, 2, 1, np.array([2, 1, 0]))
+    assert t_bad[:, 0].tolist() == [0, 1, 0] and mx_bad == pytest.approx(0.4)
+
+
+def test_multistart_keeps_the_earliest_of_equal_starts():
+    p = np.array([0.4, 0.3, 0.2, 0.1])
+    _, _, _, _, best = oracle.tid2eid_multistart(p, 2, 1, [[0, 1, 2, 3]] * 3)
+    assert best == 0
+
+
+def test_multistart_is_never_worse_than_any_start():
+    rng = np.random.default_rng(2)
+    p = rng.dirichlet(np.ones(200) * 0.3)
+    orders = [rng.permutation(200) for _ in range(6)]
+    _, f, mx, _, best = oracle.tid2eid_multistart(p, 8, 2, orders)
+    for o in orders:
+        assert mx <= oracle.tid2eid_greedy_order(p, 8, 2, o)[2]
+    assert f.sum() == pytest.approx(p.sum())
