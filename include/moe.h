@@ -67,7 +67,9 @@ typedef enum {                /* affinity s = f(z) of the logits z             *
 
 typedef enum {
   MOE_ROUTE_LEARNED = 0,      /* gate GEMM + affinity + bias + group top-k     */
-  MOE_ROUTE_HASH = 1          /* indices = tid2eid[token_id]                   */
+  MOE_ROUTE_HASH = 1,         /* indices = tid2eid[token_id]                   */
+  MOE_ROUTE_NGRAM_HASH = 2    /* 2-gram hash: token_ids holds [T, 2] pairs
+                                 (previous id, current id); see moe_route     */
 } moe_route_mode;
 
 typedef enum {
@@ -96,7 +98,8 @@ typedef struct {
   int32_t renormalize;         /* -1: renormalise iff score_func != softmax; 0/1 */
   float swiglu_limit;          /* L > 0 clamps; 0 = no clamp                     */
   int32_t route_mode;          /* moe_route_mode                                 */
-  int64_t vocab_size;          /* hash routing: rows of tid2eid                  */
+  int64_t vocab_size;          /* hash routing: rows of tid2eid; 2-gram hash:
+                                  the vocabulary size m (1 .. 2^31 - 1)          */
   int32_t act_dtype;           /* x, y, gate weight, shared expert: F32 or BF16  */
   int32_t expert_dtype;        /* routed experts: F32 (act F32), BF16 or
                                   FP4_E2M1 (act BF16)                            */
@@ -203,18 +206,63 @@ int moe_build_tid2eid(const double *p, int64_t m, int32_t n, int32_t k,
 int moe_pack_weights(const moe_config *cfg, const moe_weights *src,
                      const moe_weights *dst, void *stream);
 
+/* Multi-start variant of moe_build_tid2eid (same page, "Reference
+ * implementation": tokens taken in a random order instead of by decreasing
+ * frequency; several runs; the table with the lowest max_vio is kept).
+ *   orders      (host) [n_starts, m] int64: each row a permutation of
+ *               0..m-1, the order one run takes the tokens in (the caller
+ *               draws them, e.g. with its own seeded generator)
+ *   best_start  (host) out: row of `orders` whose table is returned (equal
+ *               max_vio keeps the earlier row), or NULL
+ * Other arguments and tie rules as moe_build_tid2eid.  Returns
+ * MOE_ERR_INVALID_ARG for n_starts < 1, a NULL `orders` or a row that is not
+ * a permutation. */
+int moe_build_tid2eid_multistart(const double *p, int64_t m, int32_t n, int32_t k,
+                                 const int64_t *orders, int32_t n_starts, int32_t *tid2eid,
+                                 double *load, double *max_vio, double *min_vio,
+                                 int32_t *best_start);
+
+/* Auxiliary-loss-free bias update ("From One Giant FFN to 384 Tiny Experts",
+ * Ch.6 and 7.1), run once per training step after a forward pass:
+ *   counts  [E] int32 pairs routed to each expert in the batch (the
+ *           forward's workspace `counts`)
+ *   T       tokens in the batch; the balanced level is T * k / E
+ *   gamma   update speed (V3: 0.001)
+ *   bias    [E] fp32 selection bias, updated in place: experts above the
+ *           balanced level get bias - gamma, experts below it bias + gamma,
+ *           experts exactly at it keep their bias (compared exactly as
+ *           counts[e] * E against T * k; each step is one fp32 operation)
+ *   stats   [4] double out, or NULL: mean load, population variance of the
+ *           counts, max_vio = max(counts) * E / (T * k) - 1 and min_vio
+ *           likewise (the balance measures of the tid2eid page and the
+ *           load-variance table of the MaxText pull request "Load balancing
+ *           changes for Deepseek v4")
+ * Returns MOE_ERR_INVALID_ARG for a NULL cfg/counts/bias, T < 1 or a
+ * non-finite gamma. */
+int moe_update_bias(const moe_config *cfg, const int32_t *counts, int64_t T, float gamma,
+                    float *bias, double *stats, void *stream);
+
 /* Workspace needed by moe_forward for T tokens, and where each part lives.
  * Host-only; layout may be NULL.  Returns MOE_OK or a validation error. */
 int moe_workspace_layout(const moe_config *cfg, int64_t T,
                          moe_ws_layout *layout);
 size_t moe_workspace_size(const moe_config *cfg, int64_t T); /* 0 if invalid */
 
-/* Routing ("gate-forward" excerpt; hash rule of Ch.11.1).
+/* Routing ("gate-forward" excerpt; hash rule of Ch.11.1; the 2-gram hash
+ * of "How was DeepSeek V4's tid2eid derived?", section "An extreme case").
  *   x         [T, dim] act_dtype (learned routing; may be NULL for hash)
- *   token_ids [T] int32 (hash routing; ignored for learned)
+ *   token_ids hash: [T] int32 token ids; 2-gram hash: [T, 2] int32 pairs
+ *             (previous token id or -1 at a sequence start, current id);
+ *             ignored for learned routing
  *   weights   [T, k] float out: gate values (hash: route_scale / k)
  *   indices   [T, k] int32 out: expert ids, in descending biased-score
- *             order; equal scores go to the lower expert id
+ *             order; equal scores go to the lower expert id.  2-gram hash:
+ *             expert j = (a * q_j + b) mod E for the pair (a, b), q_j the
+ *             j-th smallest prime above vocab_size, a = vocab_size at a
+ *             sequence start; the same expert may appear more than once.
+ *             Ids outside [0, vocab_size) route like token 0 (2-gram: like
+ *             the pair (vocab_size, 0)) with weight 0 and set
+ *             MOE_FLAG_TOKEN_ID_RANGE in the forward's flags
  * The score GEMM, affinity, bias, group limit, top-k and renormalisation run
  * in one kernel; logits never leave the chip. */
 int moe_route(const moe_config *cfg, const moe_weights *w, const void *x,

@@ -29,7 +29,7 @@ MOE_FLAG_EXPERT_RANGE = 2
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout",
     "moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_profiled",
-    "moe_pack_weights",
+    "moe_pack_weights", "moe_build_tid2eid_multistart", "moe_update_bias",
 )
 MOE_STAGES = ("route", "permute", "gemm1", "gemm2", "combine")
 
@@ -78,10 +78,13 @@ def _load():
     lib.moe_permute.argtypes = [cfgp, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_forward.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t, vp]
     lib.moe_pack_weights.argtypes = [cfgp, wp, wp, vp]
+    lib.moe_build_tid2eid_multistart.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, vp]
+    lib.moe_update_bias.argtypes = [cfgp, vp, i64, ctypes.c_float, vp, vp, vp]
     lib.moe_forward_profiled.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t,
                                          ctypes.POINTER(ctypes.c_void_p), vp]
     for f in ("moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout", "moe_route",
-              "moe_permute", "moe_forward", "moe_forward_profiled", "moe_pack_weights"):
+              "moe_permute", "moe_forward", "moe_forward_profiled", "moe_pack_weights",
+              "moe_build_tid2eid_multistart", "moe_update_bias"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -150,6 +153,29 @@ def moe_build_tid2eid(p, n: int, k: int):
     _check(_lib.moe_build_tid2eid(_ptr(p), m, n, k, _ptr(table), _ptr(load), ctypes.byref(mx),
                                   ctypes.byref(mn)), "moe_build_tid2eid")
     return table, load, mx.value, mn.value
+
+
+def moe_build_tid2eid_multistart(p, n: int, k: int, orders):
+    """Multi-start greedy on the host.  orders: int64 [S, m] token orders.
+    Returns (tid2eid, load, max_vio, min_vio, best_start)."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    orders = np.ascontiguousarray(orders, dtype=np.int64)
+    m = p.shape[0]
+    table = np.empty((m, k), dtype=np.int32)
+    load = np.empty(n, dtype=np.float64)
+    mx, mn, best = ctypes.c_double(), ctypes.c_double(), ctypes.c_int32()
+    _check(_lib.moe_build_tid2eid_multistart(_ptr(p), m, n, k, _ptr(orders), orders.shape[0],
+                                             _ptr(table), _ptr(load), ctypes.byref(mx),
+                                             ctypes.byref(mn), ctypes.byref(best)),
+           "moe_build_tid2eid_multistart")
+    return table, load, mx.value, mn.value, best.value
+
+
+def moe_update_bias(cfg: MoEConfig, counts, T: int, gamma: float, bias, stats=None, stream=None):
+    """Sign step of the selection bias (device tensors; bias updated in place;
+    stats: float64 [4] device tensor or None)."""
+    _check(_lib.moe_update_bias(ctypes.byref(config_c(cfg)), _ptr(counts), T, gamma, _ptr(bias),
+                                _ptr(stats), _stream(stream)), "moe_update_bias")
 
 
 def moe_workspace_layout(cfg: MoEConfig, T: int) -> dict:

@@ -8,7 +8,7 @@ Field names follow the model arguments of the "gate-init" excerpt on
 from dataclasses import dataclass, field, replace
 
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
-ROUTE = {"learned": 0, "hash": 1}
+ROUTE = {"learned": 0, "hash": 1, "ngram": 2}
 DTYPE = {"f32": 0, "bf16": 1, "fp4": 2}
 LAYOUT = {"rows": 0, "tiled": 1}
 
@@ -51,6 +51,7 @@ class Workload:
     x_scale: float = 1.0         # x ~ N(0, x_scale^2)
     seed: int = 0
     x_rows: int = 0              # draw x with this many rows, keep the first T
+    seq_len: int = 0             # 2-gram hash: tokens per sequence (0: one sequence)
     description: str = ""
 
 
@@ -86,12 +87,25 @@ V41_FLASH_FP4 = Workload(
     T=8192, description="V4.1-Flash shape, T=8192, d=5120, 384 experts top-8, sqrt(softplus), "
                         "FP4 e2m1 + e8m0/32 routed experts, clamp 10")
 
-FULL_WORKLOADS = {w.name: w for w in (TINY_FP32, HASH_BF16, V3_PREFILL, V3_DECODE, V41_FLASH_FP4)}
+NGRAM_BF16 = Workload(
+    "ngram_bf16",
+    replace(HASH_BF16.cfg, route_mode="ngram"),
+    T=4096, seq_len=512,
+    description="2-gram hash routing (previous id, id) -> (a*q_j + b) mod 64, 8 sequences of 512 "
+                "Zipf(1.1) ids, d=2048, I=1024, bf16")
+
+FULL_WORKLOADS = {w.name: w for w in (TINY_FP32, HASH_BF16, V3_PREFILL, V3_DECODE, V41_FLASH_FP4,
+                                      NGRAM_BF16)}
 
 # Reduced versions: the same structure at sizes the oracle finishes in
 # seconds while still spanning several GEMM tiles, slabs and a ragged tail.
 SMALL_WORKLOADS = {
     "tiny_fp32": TINY_FP32,
+    "ngram_small": Workload(
+        "ngram_small",
+        replace(HASH_BF16.cfg, dim=256, moe_inter_dim=128, n_routed_experts=16, vocab_size=2048,
+                route_mode="ngram"),
+        T=301, seq_len=64),
     "hash_small": Workload(
         "hash_small",
         replace(HASH_BF16.cfg, dim=256, moe_inter_dim=128, n_routed_experts=16, vocab_size=2048),

@@ -21,6 +21,17 @@ size_t route_logits_floats(const moe_config &cfg, int64_t T);
 hipError_t launch_dense_logits(const void *x, const void *w, int64_t T, int d, int E, float *z,
                                hipStream_t s);
 
+// 2-gram hash routing: pairs [T, 2] (previous id, current id); primes
+// [k] the k smallest primes above cfg.vocab_size.
+hipError_t launch_route_ngram(const moe_config &cfg, const int32_t *pairs, const int64_t *primes,
+                              int64_t T, float *weights, int32_t *indices, uint32_t *flags,
+                              hipStream_t s);
+
+// Sign update of the selection bias from the batch's expert counts, plus
+// load statistics (stats may be null).
+hipError_t launch_update_bias(const int32_t *counts, int E, int64_t T, int k, float gamma,
+                              float *bias, double *stats, hipStream_t s);
+
 // Hash routing: indices = tid2eid[token_id], weights = route_scale / k.
 hipError_t launch_route_hash(const moe_config &cfg, const int32_t *token_ids,
                              const int32_t *tid2eid, int64_t T, float *weights,

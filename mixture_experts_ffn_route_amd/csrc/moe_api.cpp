@@ -31,7 +31,8 @@ int validate(const moe_config *c) {
   if (G > 1 && (int64_t)k > (int64_t)c->n_limited_groups * (E / G)) return MOE_ERR_INVALID_ARG;
   if (c->score_func < MOE_SCORE_SOFTMAX || c->score_func > MOE_SCORE_SQRTSOFTPLUS)
     return MOE_ERR_INVALID_ARG;
-  if (c->route_mode != MOE_ROUTE_LEARNED && c->route_mode != MOE_ROUTE_HASH)
+  if (c->route_mode != MOE_ROUTE_LEARNED && c->route_mode != MOE_ROUTE_HASH &&
+      c->route_mode != MOE_ROUTE_NGRAM_HASH)
     return MOE_ERR_INVALID_ARG;
   if (c->renormalize < -1 || c->renormalize > 1) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->route_scale)) return MOE_ERR_INVALID_ARG;
@@ -54,6 +55,8 @@ int validate(const moe_config *c) {
   if (k > 16 || E > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->route_mode == MOE_ROUTE_HASH) {
     if (c->vocab_size < 1) return MOE_ERR_INVALID_ARG;
+  } else if (c->route_mode == MOE_ROUTE_NGRAM_HASH) {
+    if (c->vocab_size < 1 || c->vocab_size > INT32_MAX) return MOE_ERR_INVALID_ARG;
   } else {
     if (E > 512) return MOE_ERR_UNSUPPORTED;
     if (G > 1) {
@@ -109,6 +112,55 @@ int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The k smallest primes above m (trial division; m < 2^31, k <= 16).
+void primes_above(int64_t m, int k, int64_t *out) {
+  int have = 0;
+  for (int64_t q = m + 1; have < k; ++q) {
+    bool prime = q >= 2;
+    for (int64_t d = 2; prime && d * d <= q; ++d)
+      if (q % d == 0) prime = false;
+    if (prime) out[have++] = q;
+  }
+}
+
+// The greedy least-loaded rule over tokens in `order` (tid2eid page,
+// "Reference implementation"); writes table rows and returns the loads.
+void greedy_in_order(const double *p, const int64_t *order, int64_t m, int32_t n, int32_t k,
+                     int32_t *tid2eid, std::vector<double> &f) {
+  f.assign(n, 0.0);
+  std::vector<int32_t> pick(k);
+  for (int64_t oi = 0; oi < m; ++oi) {
+    const int64_t i = order[oi];
+    // k smallest (load, id) pairs, kept sorted ascending by insertion
+    int have = 0;
+    for (int32_t j = 0; j < n; ++j) {
+      const double fj = f[j];
+      if (have == k && !(fj < f[pick[k - 1]])) continue;   // ids ascend: equal load loses
+      int pos = have < k ? have : k - 1;
+      while (pos > 0 && fj < f[pick[pos - 1]]) {
+        pick[pos] = pick[pos - 1];
+        --pos;
+      }
+      pick[pos] = j;
+      if (have < k) ++have;
+    }
+    const double share = p[i] / (double)k;
+    for (int q = 0; q < k; ++q) {
+      f[pick[q]] += share;
+      tid2eid[i * k + q] = pick[q];
+    }
+  }
+}
+
+void max_min(const std::vector<double> &f, double *mx, double *mn) {
+  *mx = f[0];
+  *mn = f[0];
+  for (size_t j = 1; j < f.size(); ++j) {
+    *mx = std::max(*mx, f[j]);
+    *mn = std::min(*mn, f[j]);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,33 +187,10 @@ int moe_build_tid2eid(const double *p, int64_t m, int32_t n, int32_t k, int32_t 
   std::vector<int64_t> order(m);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(), [p](int64_t a, int64_t b) { return p[a] > p[b]; });
-  std::vector<double> f(n, 0.0);
-  std::vector<int32_t> pick(k);
-  for (int64_t i : order) {
-    // k smallest (load, id) pairs, kept sorted ascending by insertion
-    int have = 0;
-    for (int32_t j = 0; j < n; ++j) {
-      const double fj = f[j];
-      if (have == k && !(fj < f[pick[k - 1]])) continue;   // ids ascend: equal load loses
-      int pos = have < k ? have : k - 1;
-      while (pos > 0 && fj < f[pick[pos - 1]]) {
-        pick[pos] = pick[pos - 1];
-        --pos;
-      }
-      pick[pos] = j;
-      if (have < k) ++have;
-    }
-    const double share = p[i] / (double)k;
-    for (int q = 0; q < k; ++q) {
-      f[pick[q]] += share;
-      tid2eid[i * k + q] = pick[q];
-    }
-  }
-  double mx = f[0], mn = f[0];
-  for (int32_t j = 1; j < n; ++j) {
-    mx = std::max(mx, f[j]);
-    mn = std::min(mn, f[j]);
-  }
+  std::vector<double> f;
+  greedy_in_order(p, order.data(), m, n, k, tid2eid, f);
+  double mx, mn;
+  max_min(f, &mx, &mn);
   if (load) std::copy(f.begin(), f.end(), load);
   if (max_vio) *max_vio = mx * n - 1.0;
   if (min_vio) *min_vio = mn * n - 1.0;
@@ -177,6 +206,58 @@ size_t moe_workspace_size(const moe_config *cfg, int64_t T) {
   return make_layout(cfg, T, &l) == MOE_OK ? l.total_bytes : 0;
 }
 
+int moe_build_tid2eid_multistart(const double *p, int64_t m, int32_t n, int32_t k,
+                                 const int64_t *orders, int32_t n_starts, int32_t *tid2eid,
+                                 double *load, double *max_vio, double *min_vio,
+                                 int32_t *best_start) {
+  if (!p || !tid2eid || !orders || m < 1 || n < 1 || k < 1 || k > n || n_starts < 1)
+    return MOE_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < m; ++i)
+    if (!(p[i] >= 0.0) || std::isinf(p[i])) return MOE_ERR_INVALID_ARG;
+  std::vector<char> seen(m);
+  for (int32_t s = 0; s < n_starts; ++s) {
+    std::fill(seen.begin(), seen.end(), 0);
+    for (int64_t i = 0; i < m; ++i) {
+      const int64_t v = orders[s * m + i];
+      if (v < 0 || v >= m || seen[v]) return MOE_ERR_INVALID_ARG;
+      seen[v] = 1;
+    }
+  }
+  std::vector<int32_t> table((size_t)m * k);
+  std::vector<double> f, best_f;
+  double best_mx = 0.0;
+  int32_t best = -1;
+  for (int32_t s = 0; s < n_starts; ++s) {
+    greedy_in_order(p, orders + s * m, m, n, k, table.data(), f);
+    double mx, mn;
+    max_min(f, &mx, &mn);
+    const double vio = mx * n - 1.0;
+    if (best < 0 || vio < best_mx) {
+      best = s;
+      best_mx = vio;
+      best_f = f;
+      std::copy(table.begin(), table.end(), tid2eid);
+    }
+  }
+  double mx, mn;
+  max_min(best_f, &mx, &mn);
+  if (load) std::copy(best_f.begin(), best_f.end(), load);
+  if (max_vio) *max_vio = mx * n - 1.0;
+  if (min_vio) *min_vio = mn * n - 1.0;
+  if (best_start) *best_start = best;
+  return MOE_OK;
+}
+
+int moe_update_bias(const moe_config *cfg, const int32_t *counts, int64_t T, float gamma,
+                    float *bias, double *stats, void *stream) {
+  const int st = validate(cfg);
+  if (st != MOE_OK) return st;
+  if (!counts || !bias || T < 1 || !std::isfinite(gamma)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_update_bias(counts, cfg->n_routed_experts, T,
+                                            cfg->n_activated_experts, gamma, bias, stats,
+                                            (hipStream_t)stream));
+}
+
 int moe_route(const moe_config *cfg, const moe_weights *w, const void *x,
               const int32_t *token_ids, int64_t T, float *weights, int32_t *indices,
               void *stream) {
@@ -190,6 +271,12 @@ int moe_route(const moe_config *cfg, const moe_weights *w, const void *x,
     if (!token_ids || !w->tid2eid) return MOE_ERR_INVALID_ARG;
     return hip_status(moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, weights, indices,
                                              nullptr, s));
+  }
+  if (cfg->route_mode == MOE_ROUTE_NGRAM_HASH) {
+    if (!token_ids) return MOE_ERR_INVALID_ARG;
+    int64_t q[16];
+    primes_above(cfg->vocab_size, cfg->n_activated_experts, q);
+    return hip_status(moe::launch_route_ngram(*cfg, token_ids, q, T, weights, indices, nullptr, s));
   }
   if (!x || !w->gate_w) return MOE_ERR_INVALID_ARG;
   return hip_status(
@@ -225,6 +312,8 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
     return MOE_ERR_INVALID_ARG;
   if (cfg->route_mode == MOE_ROUTE_HASH) {
     if (!token_ids || !w->tid2eid) return MOE_ERR_INVALID_ARG;
+  } else if (cfg->route_mode == MOE_ROUTE_NGRAM_HASH) {
+    if (!token_ids) return MOE_ERR_INVALID_ARG;
   } else if (!w->gate_w) {
     return MOE_ERR_INVALID_ARG;
   }
@@ -246,13 +335,19 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   float *logits = (float *)(base + L.route_logits);
   int32_t *perm_hist = (int32_t *)(base + L.perm_hist);
   const int k = cfg->n_activated_experts;
-  const bool hash = cfg->route_mode == MOE_ROUTE_HASH;
+  const bool hash = cfg->route_mode != MOE_ROUTE_LEARNED;
 
   hipError_t e;
   if (events && hipEventRecord(events[MOE_STAGE_ROUTE], s) != hipSuccess) return MOE_ERR_HIP;
   if (hash) {
     if ((e = moe::launch_clear_flags(flags, s)) != hipSuccess) return MOE_ERR_HIP;
-    e = moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, route_w, route_idx, flags, s);
+    if (cfg->route_mode == MOE_ROUTE_NGRAM_HASH) {
+      int64_t q[16];
+      primes_above(cfg->vocab_size, k, q);
+      e = moe::launch_route_ngram(*cfg, token_ids, q, T, route_w, route_idx, flags, s);
+    } else {
+      e = moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, route_w, route_idx, flags, s);
+    }
   } else {
     e = moe::launch_route_learned(*cfg, x, w->gate_w, w->gate_bias, T, route_w, route_idx, s,
                                   moe::route_logits_floats(*cfg, T) ? logits : nullptr);

@@ -14,6 +14,8 @@
 // Hash gate (Ch.11.1; "How was DeepSeek V4's tid2eid derived?"): a gather of
 // tid2eid rows with uniform weights.
 
+#include <climits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -387,6 +389,98 @@ __global__ __launch_bounds__(256) void route_hash(const int32_t *token_ids, cons
   indices[p] = tid2eid[(ok ? id : 0) * k + j];
   weights[p] = ok ? wval : 0.f;
   if (!ok && flags) atomicOr(flags, (uint32_t)MOE_FLAG_TOKEN_ID_RANGE);
+}
+
+// 2-gram hash ("How was DeepSeek V4's tid2eid derived?", section "An extreme
+// case"): one thread per (token, slot); expert = (a * q_j + b) mod E in
+// 64-bit integers.
+struct NgramPrimes { int64_t q[16]; };
+
+__global__ __launch_bounds__(256) void route_ngram(const int32_t *pairs, NgramPrimes primes,
+                                                   int64_t T, int k, int E, int64_t vocab,
+                                                   float wval, float *weights, int32_t *indices,
+                                                   uint32_t *flags) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= T * k) return;
+  const int64_t t = p / k;
+  const int j = (int)(p - t * k);
+  const int64_t prev = pairs[2 * t], cur = pairs[2 * t + 1];
+  const bool ok = prev >= -1 && prev < vocab && cur >= 0 && cur < vocab;
+  const int64_t a = ok ? (prev < 0 ? vocab : prev) : vocab;
+  const int64_t b = ok ? cur : 0;
+  indices[p] = (int32_t)((a * primes.q[j] + b) % E);
+  weights[p] = ok ? wval : 0.f;
+  if (!ok && flags) atomicOr(flags, (uint32_t)MOE_FLAG_TOKEN_ID_RANGE);
+}
+
+hipError_t launch_route_ngram(const moe_config &cfg, const int32_t *pairs, const int64_t *primes,
+                              int64_t T, float *weights, int32_t *indices, uint32_t *flags,
+                              hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int k = cfg.n_activated_experts;
+  NgramPrimes q = {};
+  for (int j = 0; j < k; ++j) q.q[j] = primes[j];
+  const int64_t n = T * k;
+  hipLaunchKernelGGL(route_ngram, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pairs, q,
+                     T, k, cfg.n_routed_experts, cfg.vocab_size, cfg.route_scale / (float)k,
+                     weights, indices, flags);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Bias update ("From One Giant FFN to 384 Tiny Experts", Ch.6): one
+// workgroup; experts strided over the threads; the statistics reduce in a
+// fixed order (per-wave shuffles, then wave 0 over the waves).
+__global__ __launch_bounds__(1024) void update_bias_kernel(const int32_t *counts, int E, int64_t T,
+                                                           int k, float gamma, float *bias,
+                                                           double *stats) {
+  __shared__ double ssq[16];
+  __shared__ int smax[16], smin[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t total = T * k;
+  const double mean = (double)total / E;
+  double sq = 0.0;
+  int mx = INT_MIN, mn = INT_MAX;
+  for (int e = tid; e < E; e += 1024) {
+    const int c = counts[e];
+    const int64_t lhs = (int64_t)c * E;
+    if (lhs > total) bias[e] = bias[e] - gamma;
+    else if (lhs < total) bias[e] = bias[e] + gamma;
+    const double dv = (double)c - mean;
+    sq += dv * dv;
+    mx = c > mx ? c : mx;
+    mn = c < mn ? c : mn;
+  }
+  if (!stats) return;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    sq += __shfl_xor(sq, off);
+    const int omx = __shfl_xor(mx, off), omn = __shfl_xor(mn, off);
+    mx = omx > mx ? omx : mx;
+    mn = omn < mn ? omn : mn;
+  }
+  if (lane == 0) { ssq[w] = sq; smax[w] = mx; smin[w] = mn; }
+  __syncthreads();
+  if (tid == 0) {
+    double s = 0.0;
+    int gmx = INT_MIN, gmn = INT_MAX;
+    for (int i = 0; i < 16; ++i) {
+      s += ssq[i];
+      gmx = smax[i] > gmx ? smax[i] : gmx;
+      gmn = smin[i] < gmn ? smin[i] : gmn;
+    }
+    stats[0] = mean;
+    stats[1] = s / E;
+    stats[2] = (double)((int64_t)gmx * E) / (double)total - 1.0;
+    stats[3] = (double)((int64_t)gmn * E) / (double)total - 1.0;
+  }
+}
+
+hipError_t launch_update_bias(const int32_t *counts, int E, int64_t T, int k, float gamma,
+                              float *bias, double *stats, hipStream_t s) {
+  hipLaunchKernelGGL(update_bias_kernel, dim3(1), dim3(1024), 0, s, counts, E, T, k, gamma, bias,
+                     stats);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

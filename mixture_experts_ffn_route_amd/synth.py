@@ -102,6 +102,9 @@ def make_layer(workload, device):
 
     Keys: x, gate_w, gate_bias, w_gate, w_up, w_down, s_gate, s_up, s_down,
     sh_gate, sh_up, sh_down, token_ids, p (numpy float64, hash only).
+    2-gram hash layers get token_ids [T, 2] = (previous id, current id): the
+    batch is T / seq_len sequences of Zipf-sampled ids, and the first
+    position of each sequence has previous id -1.
     Missing members are None.  workload.x_rows > T draws x with that many
     rows and keeps the first T (decode reuses the prefill batch's first rows).
     """
@@ -121,7 +124,13 @@ def make_layer(workload, device):
     else:
         p = zipf_probs(cfg.vocab_size, workload.zipf_s)
         out["p"] = p
-        out["token_ids"] = torch.from_numpy(sample_token_ids(p, T, seed)).to(device)
+        ids = sample_token_ids(p, T, seed)
+        if cfg.route_mode == "ngram":
+            L = workload.seq_len or T
+            prev = np.concatenate([[-1], ids[:-1]]).astype(np.int32)
+            prev[::L] = -1
+            ids = np.stack([prev, ids], axis=1)
+        out["token_ids"] = torch.from_numpy(np.ascontiguousarray(ids)).to(device)
 
     shapes = {"w_gate": (I, d), "w_up": (I, d), "w_down": (d, I)}
     for name, (n_out, n_in) in shapes.items():

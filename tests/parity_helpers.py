@@ -48,6 +48,14 @@ def oracle_route(cfg, layer, tid2eid_oracle=None, rows=None):
             ids = ids[rows]
         w, idx = oracle.hash_gate(ids, tid2eid_oracle, cfg.route_scale)
         return w, idx, None
+    if cfg.route_mode == "ngram":
+        pairs = cpu_np(layer["token_ids"]).astype(np.int64)
+        if rows is not None:
+            pairs = pairs[rows]
+        w, idx = oracle.ngram_hash_gate(pairs[:, 0], pairs[:, 1], cfg.vocab_size,
+                                        cfg.n_routed_experts, cfg.n_activated_experts,
+                                        cfg.route_scale)
+        return w, idx, None
     x = f64(layer["x"]) if rows is None else f64(layer["x"][torch.as_tensor(rows)])
     bias = None if layer["gate_bias"] is None else cpu_np(layer["gate_bias"])
     return oracle.learned_gate(

@@ -199,3 +199,46 @@ def test_tid2eid_builder_rejects_bad_input():
         B.moe_build_tid2eid(np.array([0.5, -0.1]), 4, 2)
     with pytest.raises(B.MoEError):
         B.moe_build_tid2eid(np.array([0.5, 0.5]), 2, 3)
+
+
+def test_multistart_builder_matches_oracle():
+    rng = np.random.default_rng(21)
+    m, n, k = 3000, 32, 4
+    p = rng.dirichlet(np.ones(m) * 0.5)
+    orders = np.stack([rng.permutation(m) for _ in range(5)])
+    table, load, mx, mn, best = B.moe_build_tid2eid_multistart(p, n, k, orders)
+    ot, of, omx, omn, obest = oracle.tid2eid_multistart(p, n, k, orders)
+    assert best == obest
+    np.testing.assert_array_equal(table, ot)
+    np.testing.assert_allclose(load, of, rtol=0, atol=0)
+    assert (mx, mn) == (omx, omn)
+
+
+def test_multistart_builder_rejects_bad_orders():
+    p = np.full(4, 0.25)
+    with pytest.raises(B.MoEError):
+        B.moe_build_tid2eid_multistart(p, 2, 1, [[0, 1, 2, 2]])      # not a permutation
+    with pytest.raises(B.MoEError):
+        B.moe_build_tid2eid_multistart(p, 2, 1, [[0, 1, 2, 4]])      # out of range
+    with pytest.raises(B.MoEError):
+        B.moe_build_tid2eid_multistart(p, 2, 1, np.zeros((0, 4), dtype=np.int64))
+
+
+def test_update_bias_and_ngram_checks_before_any_launch():
+    fake = ctypes.c_void_p(0x100000)
+    cc = B.config_c(V3)
+    ub = B._lib.moe_update_bias
+    assert ub(None, fake, 16, ctypes.c_float(0.001), fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(cc), None, 16, ctypes.c_float(0.001), fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(cc), fake, 16, ctypes.c_float(0.001), None, None, None) == B.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(cc), fake, 0, ctypes.c_float(0.001), fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert ub(ctypes.byref(cc), fake, 16, ctypes.c_float(float("nan")), fake, None,
+              None) == B.MOE_ERR_INVALID_ARG
+    ng = C.NGRAM_BF16.cfg
+    assert B.moe_validate_config(ng) == B.MOE_OK
+    assert B.moe_validate_config(replace(ng, vocab_size=0)) == B.MOE_ERR_INVALID_ARG
+    assert B.moe_validate_config(replace(ng, vocab_size=1 << 31)) == B.MOE_ERR_INVALID_ARG
+    # the 2-gram forward needs its pair table
+    full = B.MoeWeightsC(*([fake] * 12))
+    assert B._lib.moe_forward(ctypes.byref(B.config_c(ng)), ctypes.byref(full), fake, None, 8,
+                              ctypes.c_void_p(0x200000), fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG

@@ -1,0 +1,91 @@
+"""GPU parity of moe_update_bias (the auxiliary-loss-free bias step of "From
+One Giant FFN to 384 Tiny Experts", Ch.6) and of the 2-gram hash route's
+range flag.  Bias updates are bit-exact against the oracle (one fp32 step per
+expert, decided by an exact integer comparison); the load statistics to
+1e-12 relative."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dataclasses import replace
+from mixture_experts_ffn_route_amd import binding as B
+from mixture_experts_ffn_route_amd import config as C
+from mixture_experts_ffn_route_amd import synth
+from tests import parity_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("E,T,k,gamma,seed", [(256, 4096, 8, 0.001, 0), (384, 8192, 8, 0.001, 1),
+                                              (1024, 700, 3, 0.01, 2), (7, 5, 3, 0.5, 3),
+                                              (64, 4096, 4, 0.0, 4)])
+def test_update_bias_matches_oracle(E, T, k, gamma, seed, gpu):
+    rng = np.random.default_rng(seed)
+    counts = rng.multinomial(T * k, rng.dirichlet(np.ones(E))).astype(np.int32)
+    # a few experts exactly at the balanced level when it is an integer
+    if (T * k) % E == 0:
+        lvl = T * k // E
+        counts[:3] = lvl
+        counts[3] = T * k - counts[:3].sum() - counts[4:].sum()
+        counts = np.maximum(counts, 0)
+    bias = rng.uniform(-0.01, 0.01, size=E).astype(np.float32)
+    cfg = C.MoEConfig(dim=64, n_routed_experts=E, n_activated_experts=k, moe_inter_dim=64,
+                      route_mode="hash", vocab_size=1)
+    dev_bias = torch.from_numpy(bias.copy()).to(gpu)
+    stats = torch.zeros(4, dtype=torch.float64, device=gpu)
+    print(f"[bias] E={E} T={T} k={k}", flush=True)
+    B.moe_update_bias(cfg, torch.from_numpy(counts).to(gpu), T, gamma, dev_bias, stats)
+    torch.cuda.synchronize()
+    want = oracle.bias_update(bias, counts, T, k, gamma)
+    np.testing.assert_array_equal(H.cpu_np(dev_bias).view(np.uint32), want.view(np.uint32))
+    np.testing.assert_allclose(H.cpu_np(stats), oracle.load_stats(counts, T, k), rtol=1e-12,
+                               atol=1e-15)
+
+
+def test_bias_step_after_a_forward(gpu):
+    """The training-time sequence on one stream: forward, then a bias step
+    from the forward's counts; routing and counts match the oracle, and so
+    does the updated bias."""
+    wl = C.SMALL_WORKLOADS["v3_small"]
+    cfg, T = wl.cfg, wl.T
+    layer = synth.make_layer(wl, gpu)
+    ws = B.alloc_workspace(cfg, T, gpu)
+    y = torch.empty_like(layer["x"])
+    bias0 = layer["gate_bias"].clone()
+    B.moe_forward(cfg, layer, layer["x"], None, T, y, ws)
+    v = B.workspace_views(cfg, T, ws)
+    bias = bias0.clone()
+    B.moe_update_bias(cfg, v["counts"], T, 0.001, bias)
+    torch.cuda.synchronize()
+    ow, oidx, aux = H.oracle_route(cfg, layer)
+    differ = H.compare_routing(cfg, H.cpu_np(v["route_weights"]), H.cpu_np(v["route_indices"]),
+                               ow, oidx, aux)
+    if differ.any():
+        pytest.skip("near-tie routing: counts not unique")
+    ocounts = np.bincount(oidx.ravel(), minlength=cfg.n_routed_experts)
+    np.testing.assert_array_equal(H.cpu_np(v["counts"]), ocounts)
+    want = oracle.bias_update(H.cpu_np(bias0), ocounts, T, cfg.n_activated_experts, 0.001)
+    np.testing.assert_array_equal(H.cpu_np(bias).view(np.uint32), want.view(np.uint32))
+
+
+def test_ngram_bad_ids_flagged(gpu):
+    wl = C.SMALL_WORKLOADS["ngram_small"]
+    cfg, T = wl.cfg, wl.T
+    layer = synth.make_layer(wl, gpu)
+    pairs = layer["token_ids"].clone()
+    pairs[7, 1] = cfg.vocab_size          # current id out of range
+    pairs[9, 0] = -2                      # previous id below the start marker
+    layer["token_ids"] = pairs
+    ws = B.alloc_workspace(cfg, T, gpu)
+    y = torch.empty_like(layer["x"])
+    B.moe_forward(cfg, layer, layer["x"], pairs, T, y, ws)
+    torch.cuda.synchronize()
+    v = B.workspace_views(cfg, T, ws)
+    assert int(v["flags"][0]) & B.MOE_FLAG_TOKEN_ID_RANGE
+    assert torch.all(v["route_weights"][7] == 0) and torch.all(v["route_weights"][9] == 0)
+    good = np.ones(T, bool)
+    good[[7, 9]] = False
+    ow, oidx, _ = H.oracle_route(cfg, {"token_ids": pairs[torch.as_tensor(good, device=gpu)]})
+    np.testing.assert_array_equal(H.cpu_np(v["route_indices"])[good], oidx)

@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 # tokens whose output the oracle recomputes (None: all of them)
 SAMPLE = {"tiny_fp32": None, "v3_decode": None, "hash_bf16": 64, "v3_prefill": 24,
-          "v41_flash_fp4": 16}
+          "v41_flash_fp4": 16, "ngram_bf16": 64}
 
 
 def _sample_rows(T, n, seed):
