@@ -48,6 +48,7 @@ struct GemmArgs {
   const float *sorted_w;     // one-matrix form: gate value of each permuted row
   int tiled;                 // B, S, SB in the tiled layout (moe_pack_weights)
   float *Cf;                 // one-matrix form: fp32 output instead of C, or null
+  int n_shared_tiles;        // leading tiles of the range that are shared-expert tiles
   int64_t dense_rows;        // tiles == null: one group of this many rows, cut
   int dense_tile_rows;       //   into tiles of dense_tile_rows rows
   int64_t routed_rows;       // T * k: rows at or above this belong to the shared expert
@@ -373,17 +374,33 @@ void grouped_gemm(const GemmArgs g) {
   constexpr int SLOT = gemm_slot_elems<WAVES, NB, NCB, MB, FP4, NS>();
   __shared__ __attribute__((aligned(1024))) bf16 As[NS * SLOT];
 
-  // ---- work item (XCD-aware) ----
+  // ---- work item (XCD-aware).  Workgroups are dealt round-robin to the 8
+  // XCDs (blockIdx & 7).  Shared-expert tiles (every one a full, compute-heavy
+  // tile whose weights all XCDs would otherwise wait on) go to the XCDs in
+  // turn, all slabs of a tile on one XCD; the routed items are then split
+  // into 8 contiguous runs, so an expert's slabs share one XCD's L2. ----
   const int tend = g.tile_end >= 0 ? g.tile_end : *g.tile_count;
-  const int64_t work = (int64_t)(tend - g.tile_begin) * g.n_slabs;
+  const int nsh = g.n_shared_tiles;
   const int xcd = blockIdx.x & 7;
   const int64_t slot = blockIdx.x >> 3;
-  const int64_t per_xcd = (work + 7) >> 3;
-  if (slot >= per_xcd) return;
-  const int64_t item = xcd * per_xcd + slot;
-  if (item >= work) return;
-  const int tile = g.tile_begin + (int)(item / g.n_slabs);
-  const int slab = (int)(item - (int64_t)(tile - g.tile_begin) * g.n_slabs);
+  const int sh_cnt = nsh > xcd ? (nsh - xcd + 7) >> 3 : 0;
+  const int64_t sh_items = (int64_t)sh_cnt * g.n_slabs;
+  int tile, slab;
+  if (slot < sh_items) {
+    const int i = (int)(slot / g.n_slabs);
+    tile = g.tile_begin + xcd + 8 * i;
+    slab = (int)(slot - (int64_t)i * g.n_slabs);
+  } else {
+    const int64_t routed = (int64_t)(tend - g.tile_begin - nsh) * g.n_slabs;
+    const int64_t r_per = (routed + 7) >> 3;
+    const int64_t r = slot - sh_items;
+    if (r >= r_per) return;
+    const int64_t item = xcd * r_per + r;
+    if (item >= routed) return;
+    const int64_t rt = item / g.n_slabs;
+    tile = g.tile_begin + nsh + (int)rt;
+    slab = (int)(item - rt * g.n_slabs);
+  }
 
   TileCtx t;
   if (g.tiles) {
@@ -548,8 +565,10 @@ static hipError_t run_gemm(const GemmArgs &a, int max_tiles, hipStream_t s) {
   if constexpr (!gemm_cfg_fits<WAVES, NB, NCB, MB, FP4, NS>()) {
     return hipErrorInvalidValue;
   } else {
-  int64_t blocks = (int64_t)max_tiles * a.n_slabs;
-  blocks = (blocks + 7) / 8 * 8;
+  // per XCD: its share of the shared tiles, then an eighth of the rest
+  const int64_t per_xcd = (int64_t)((a.n_shared_tiles + 7) / 8) * a.n_slabs +
+                          ((int64_t)(max_tiles - a.n_shared_tiles) * a.n_slabs + 7) / 8;
+  const int64_t blocks = 8 * per_xcd;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((grouped_gemm<WAVES, NB, NCB, MB, FP4, NS>), dim3((unsigned)blocks),
                      dim3(WAVES * 64), 0, s, a);
@@ -692,6 +711,7 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
       return err;
   } else {
     a.tile_begin = 0; a.tile_end = -1;
+    a.n_shared_tiles = p.n_shared_tiles;
     if ((err = gemm_launch(2, false, mb, a, p.max_tiles, s)) != hipSuccess) return err;
   }
 
@@ -716,6 +736,7 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
       return err;
   } else {
     a.tile_begin = 0; a.tile_end = -1;
+    a.n_shared_tiles = p.n_shared_tiles;
     if ((err = gemm_launch(1, false, mb, a, p.max_tiles, s)) != hipSuccess) return err;
   }
 
