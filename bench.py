@@ -63,6 +63,41 @@ def algorithmic_counts(wl, counts):
     return {"n_hit": n_hit, "gemm1": gemm1, "layer": {"flops": layer_flops, "bytes": layer_bytes}}
 
 
+def achievable_peaks(torch, B):
+    """Achievable denominators on this GPU, from the library's roofline probes
+    (the layer kernels' own instruction forms): 16-byte loads streaming a
+    4 GiB buffer, and chains of 16x16x32 bf16 MFMAs on every SIMD."""
+    dev = torch.device("cuda:0")
+    buf = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    out = torch.empty(4096, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        B.moe_probe_read(buf, out)
+        B.moe_probe_mfma(2000, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        B.moe_probe_read(buf, out)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    rates = {}
+    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+        e0.record()
+        flops = 0.0
+        for _ in range(5):
+            flops += B.moe_probe_mfma(20000 if shape == 0 else 10000, out, shape)
+        e1.record()
+        torch.cuda.synchronize()
+        rates[name] = round(flops / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
+    mfma_tflops = max(rates.values())
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round(read_gbs, 1), "bf16_mfma_tflops": mfma_tflops,
+            "bf16_mfma_tflops_by_shape": rates,
+            "how": "moe_probe_read over 4 GiB; moe_probe_mfma (2048 x 4 waves x 8 chains)"}
+
+
 def roofline_entry(flops, nbytes, seconds, peak_tflops):
     t_mfma = flops / (peak_tflops * 1e12)
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
@@ -146,6 +181,9 @@ def workload_report(wl, ms, stage_ms, counts, peak):
     layer_roof = roofline_entry(lay["flops"], lay["bytes"], ms / 1e3, peak)
     return {
         "tokens_per_s": round(wl.T / (ms / 1e3), 1),
+        # both fractions of the whole layer step (the metric asks for MFMA and HBM %)
+        "layer_mfma_frac": round(lay["flops"] / (ms / 1e3) / (peak * 1e12), 4),
+        "layer_hbm_frac": round(lay["bytes"] / (ms / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
         "ms_per_step": round(ms, 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "experts_hit": alg["n_hit"],
@@ -229,6 +267,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=96,
                     help="tokens of the batch the CPU oracle is timed on (about 10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the achievable matmul / HBM-read denominators")
     ap.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
                     help="expert weight storage the timed steps read (tiled: packed once by "
                          "moe_pack_weights before timing)")
@@ -300,7 +340,8 @@ def main():
                        "frac": g1["frac"], "traffic": load_traffic(wl.name),
                        "algorithmic_bytes": g1["bytes"], "algorithmic_flops": g1["flops"],
                        "avg_ms": g1["ms"]}
-    out["layer_roofline"] = rep["layer"]
+    out["layer_roofline"] = {**rep["layer"], "mfma_frac": rep["layer_mfma_frac"],
+                             "hbm_frac": rep["layer_hbm_frac"]}
     out["stage_ms"] = rep["stage_ms"]
 
     reports = {}
@@ -328,6 +369,14 @@ def main():
     if reports:
         out["extra_workloads"] = reports
 
+    if not args.no_peaks:
+        log("measuring achievable peaks")
+        pk = achievable_peaks(torch, B)
+        out["achievable_peaks"] = pk
+        r = out["roofline"]
+        denom = pk["hbm_read_gbs"] if r["unit"] == "GB/s" else pk["bf16_mfma_tflops"]
+        r["frac_of_achievable"] = round(r["achieved"] / denom, 4)
+        log(f"achievable: {pk}")
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_sample_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(wl, layer, args.cpu_sample_tokens)

@@ -315,6 +315,25 @@ int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void
                          const int32_t *token_ids, int64_t T, void *y,
                          void *ws, size_t ws_bytes, void **events, void *stream);
 
+/* Roofline probes: the achievable HBM read rate and bf16 MFMA rate of the
+ * GPU, measured with the instruction forms the layer kernels use (16-byte
+ * vector loads; v_mfma_f32_16x16x32_bf16), for the caller to time on
+ * `stream` and report next to the data-sheet peaks.  Neither touches the
+ * layer state.
+ *   moe_probe_read: reads `bytes` (a multiple of 16) of `buf` (16-byte
+ *     aligned); 1024 workgroups of 4 waves, each wave streaming its own
+ *     contiguous share with 1 KB loads, 8 in flight.  out: uint32 [1024]
+ *     device scratch, written only if the loaded words hash to one fixed
+ *     value (so the loads cannot be dropped).
+ *   moe_probe_mfma: 2048 workgroups x 4 waves, each wave `iters` rounds of 8
+ *     independent bf16 MFMAs, 16x16x32 (shape 0) or 32x32x16 (shape 1).
+ *     out: float [2048] device scratch, written likewise; *flops (host)
+ *     receives the flops the launch performs.
+ * Return MOE_ERR_INVALID_ARG for NULL/misaligned pointers, bytes < 16,
+ * iters < 1 or another shape. */
+int moe_probe_read(const void *buf, int64_t bytes, void *out, void *stream);
+int moe_probe_mfma(int32_t iters, int32_t shape, void *out, double *flops, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,8 @@ MOE_FLAG_EXPERT_RANGE = 2
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout",
     "moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_profiled",
-    "moe_pack_weights", "moe_build_tid2eid_multistart", "moe_update_bias",
+    "moe_pack_weights", "moe_build_tid2eid_multistart", "moe_update_bias", "moe_probe_read",
+    "moe_probe_mfma",
 )
 MOE_STAGES = ("route", "permute", "gemm1", "gemm2", "combine")
 
@@ -80,11 +81,14 @@ def _load():
     lib.moe_pack_weights.argtypes = [cfgp, wp, wp, vp]
     lib.moe_build_tid2eid_multistart.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, vp]
     lib.moe_update_bias.argtypes = [cfgp, vp, i64, ctypes.c_float, vp, vp, vp]
+    lib.moe_probe_read.argtypes = [vp, i64, vp, vp]
+    lib.moe_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
     lib.moe_forward_profiled.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t,
                                          ctypes.POINTER(ctypes.c_void_p), vp]
     for f in ("moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout", "moe_route",
               "moe_permute", "moe_forward", "moe_forward_profiled", "moe_pack_weights",
-              "moe_build_tid2eid_multistart", "moe_update_bias"):
+              "moe_build_tid2eid_multistart", "moe_update_bias", "moe_probe_read",
+              "moe_probe_mfma"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -176,6 +180,20 @@ def moe_update_bias(cfg: MoEConfig, counts, T: int, gamma: float, bias, stats=No
     stats: float64 [4] device tensor or None)."""
     _check(_lib.moe_update_bias(ctypes.byref(config_c(cfg)), _ptr(counts), T, gamma, _ptr(bias),
                                 _ptr(stats), _stream(stream)), "moe_update_bias")
+
+
+def moe_probe_read(buf, out, stream=None):
+    _check(_lib.moe_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                               _stream(stream)), "moe_probe_read")
+
+
+def moe_probe_mfma(iters: int, out, shape=0, stream=None) -> float:
+    """Launch the MFMA probe (shape 0: 16x16x32, 1: 32x32x16); returns the
+    flops the launch performs."""
+    flops = ctypes.c_double()
+    _check(_lib.moe_probe_mfma(iters, shape, _ptr(out), ctypes.byref(flops), _stream(stream)),
+           "moe_probe_mfma")
+    return flops.value
 
 
 def moe_workspace_layout(cfg: MoEConfig, T: int) -> dict:

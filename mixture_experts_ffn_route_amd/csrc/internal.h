@@ -91,4 +91,9 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s);
 hipError_t launch_pack_matrix(const void *src, void *dst, int64_t count, int64_t N, int64_t K,
                               int dtype, bool scales, hipStream_t s);
 
+// Roofline probes (moe_probe_read / moe_probe_mfma).
+hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *out, hipStream_t s);
+hipError_t launch_probe_mfma(int iters, bool big, float *out, hipStream_t s);
+int64_t probe_mfma_flops(int iters, bool big);
+
 }  // namespace moe

@@ -447,4 +447,15 @@ int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void
   return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, (hipEvent_t *)events, stream);
 }
 
+int moe_probe_read(const void *buf, int64_t bytes, void *out, void *stream) {
+  if (!buf || !out || bytes < 16 || bytes % 16 || ((uintptr_t)buf % 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_probe_read(buf, bytes, (uint32_t *)out, (hipStream_t)stream));
+}
+
+int moe_probe_mfma(int32_t iters, int32_t shape, void *out, double *flops, void *stream) {
+  if (!out || iters < 1 || (shape != 0 && shape != 1)) return MOE_ERR_INVALID_ARG;
+  if (flops) *flops = (double)moe::probe_mfma_flops(iters, shape == 1);
+  return hip_status(moe::launch_probe_mfma(iters, shape == 1, (float *)out, (hipStream_t)stream));
+}
+
 }  // extern "C"

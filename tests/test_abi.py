@@ -242,3 +242,13 @@ def test_update_bias_and_ngram_checks_before_any_launch():
     full = B.MoeWeightsC(*([fake] * 12))
     assert B._lib.moe_forward(ctypes.byref(B.config_c(ng)), ctypes.byref(full), fake, None, 8,
                               ctypes.c_void_p(0x200000), fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_probes_check_before_any_launch():
+    fake = ctypes.c_void_p(0x100000)
+    assert B._lib.moe_probe_read(None, 1 << 20, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert B._lib.moe_probe_read(fake, 8, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert B._lib.moe_probe_read(ctypes.c_void_p(0x100004), 1 << 20, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert B._lib.moe_probe_mfma(0, 0, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert B._lib.moe_probe_mfma(10, 2, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert B._lib.moe_probe_mfma(10, 0, None, None, None) == B.MOE_ERR_INVALID_ARG
