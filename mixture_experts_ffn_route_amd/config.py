@@ -144,6 +144,31 @@ SMALL_WORKLOADS = {
         MoEConfig(dim=256, n_routed_experts=48, n_activated_experts=6, moe_inter_dim=128,
                   score_func="sigmoid", route_scale=1.0, has_bias=True),
         T=1030, description="1024+ tokens with E % 64 != 0: split router, chunked permute"),
+    # limits and degenerate cases
+    "max_e512_k16": Workload(
+        "max_e512_k16",
+        MoEConfig(dim=256, n_routed_experts=512, n_activated_experts=16, moe_inter_dim=128,
+                  n_expert_groups=16, n_limited_groups=8, score_func="sigmoid", route_scale=2.5,
+                  has_bias=True),
+        T=100, description="learned routing at the largest E and k: 512 experts, 16 groups, top-16"),
+    "single_expert": Workload(
+        "single_expert",
+        MoEConfig(dim=256, n_routed_experts=1, n_activated_experts=1, moe_inter_dim=128,
+                  score_func="softmax"),
+        T=50, description="E = k = 1: every token to expert 0 with weight 1 (a dense SwiGLU)"),
+    "fp4_one_token": Workload(
+        "fp4_one_token",
+        replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48),
+        T=1),
+    "ngram_k16": Workload(
+        "ngram_k16",
+        replace(HASH_BF16.cfg, dim=256, moe_inter_dim=128, n_routed_experts=64, vocab_size=2048,
+                n_activated_experts=16, route_mode="ngram"),
+        T=130, seq_len=40, description="2-gram hash with 16 primes (duplicates frequent)"),
+    "hash_vocab1": Workload(
+        "hash_vocab1",
+        replace(HASH_BF16.cfg, dim=256, moe_inter_dim=128, n_routed_experts=16, vocab_size=1),
+        T=70, description="one-token vocabulary: every token has the same k experts"),
     "sigmoid_noshared_big_tiles": Workload(
         "sigmoid_noshared_big_tiles",
         MoEConfig(dim=320, n_routed_experts=8, n_activated_experts=2, moe_inter_dim=128,

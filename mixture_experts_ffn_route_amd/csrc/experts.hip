@@ -496,25 +496,36 @@ __global__ __launch_bounds__(256) void expert_down_f32(
 
 // ---------------------------------------------------------------------------
 // Combine: y[t] = sum_j Y[inverse[t, j]] + Y[T*k + t], fp32 sum in slot order.
+// One workgroup per token.  The token's k permuted rows (and its shared row)
+// are looked up first; then every lane issues all k+1 16-byte loads of its
+// 8 columns before adding them in slot order, shared row last (a dropped pair,
+// inverse = -1, contributes nothing).
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_bf16(const bf16 *Y, const int32_t *inverse,
                                                     int k, int dim, int64_t shared_base,
                                                     bf16 *y) {
   const int64_t t = blockIdx.x;
+  int64_t row[KMAX + 1];
+  bool use[KMAX + 1];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int r = j < k ? inverse[t * k + j] : -1;
+    use[j] = r >= 0;
+    row[j] = r >= 0 ? r : 0;
+  }
+  use[KMAX] = shared_base >= 0;
+  row[KMAX] = shared_base >= 0 ? shared_base + t : 0;
   for (int c = threadIdx.x * 8; c < dim; c += 256 * 8) {
+    bf16x8 v[KMAX + 1];
+#pragma unroll
+    for (int j = 0; j <= KMAX; ++j) v[j] = *(const bf16x8 *)(Y + row[j] * dim + c);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = inverse[t * k + j];
-      if (r >= 0) {
-        const bf16x8 v = *(const bf16x8 *)(Y + (int64_t)r * dim + c);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
+    for (int j = 0; j <= KMAX; ++j)
+      if (use[j]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += (float)v[j][i];
       }
-    }
-    if (shared_base >= 0) {
-      const bf16x8 v = *(const bf16x8 *)(Y + (shared_base + t) * dim + c);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
-    }
     bf16x8 o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = (bf16)acc[i];
@@ -741,9 +752,20 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   }
 
   if ((err = mark(p, MOE_STAGE_COMBINE, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL(combine_bf16, dim3((unsigned)p.T), dim3(256), 0, s, (const bf16 *)p.yrows,
-                     p.inverse, p.k, p.dim, p.has_shared ? routed_rows : (int64_t)-1,
-                     (bf16 *)p.y);
+  {
+    const int64_t sb = p.has_shared ? routed_rows : (int64_t)-1;
+    const dim3 grid((unsigned)p.T), blk(256);
+    const bf16 *Y = (const bf16 *)p.yrows;
+    bf16 *yo = (bf16 *)p.y;
+    if (p.k <= 2)
+      hipLaunchKernelGGL(combine_bf16<2>, grid, blk, 0, s, Y, p.inverse, p.k, p.dim, sb, yo);
+    else if (p.k <= 4)
+      hipLaunchKernelGGL(combine_bf16<4>, grid, blk, 0, s, Y, p.inverse, p.k, p.dim, sb, yo);
+    else if (p.k <= 8)
+      hipLaunchKernelGGL(combine_bf16<8>, grid, blk, 0, s, Y, p.inverse, p.k, p.dim, sb, yo);
+    else
+      hipLaunchKernelGGL(combine_bf16<16>, grid, blk, 0, s, Y, p.inverse, p.k, p.dim, sb, yo);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return mark(p, MOE_STAGE_COUNT, s);
 }
