@@ -262,7 +262,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode", default="v3_decode", help="second workload ('' to skip)")
-    ap.add_argument("--extra", default="hash_bf16,ngram_bf16,v41_flash_fp4,tiny_fp32",
+    ap.add_argument("--extra", default="hash_bf16,ngram_bf16,v41_flash_fp4,v41_flash_fp4_mx,tiny_fp32",
                     help="comma-separated further workloads to report ('' for none)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=96,
                     help="tokens of the batch the CPU oracle is timed on (about 10 s)")

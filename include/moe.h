@@ -83,6 +83,20 @@ typedef enum {
   MOE_LAYOUT_TILED = 1        /* expert matrices as written by moe_pack_weights */
 } moe_weight_layout;
 
+typedef enum {
+  MOE_ACT_QUANT_NONE = 0,     /* routed experts see the bf16 activations       */
+  MOE_ACT_QUANT_MXFP8 = 1     /* FP4 routed experts: the activations entering
+                                 each routed GEMM (gathered x; SwiGLU output H)
+                                 are quantised to OCP MXFP8 (E4M3 + one E8M0
+                                 scale per 32 inputs, shared exponent
+                                 floor(log2 amax) - 8, nearest value, ties to
+                                 even, saturating at 448) and multiplied with
+                                 the stored FP4 codes on the scaled MFMA; needs
+                                 expert_dtype FP4_E2M1, act_dtype BF16,
+                                 dim % 128 == 0, moe_inter_dim % 128 == 0.  The
+                                 shared expert keeps bf16 activations.         */
+} moe_act_quant;
+
 /* Layer configuration.  Field names follow the model arguments of the
  * "gate-init" excerpt and the V4.1 MoE class. */
 typedef struct {
@@ -105,6 +119,7 @@ typedef struct {
                                   FP4_E2M1 (act BF16)                            */
   int32_t weight_layout;       /* moe_weight_layout of the routed and shared
                                   expert matrices; TILED needs act_dtype BF16    */
+  int32_t act_quant;           /* moe_act_quant for the routed FP4 experts       */
 } moe_config;
 
 /* Layer weights; unused members may be NULL. */
@@ -142,6 +157,10 @@ typedef struct {
   size_t route_logits;         /* float          partial gate logits (learned
                                   bf16 routing; 0 bytes otherwise)               */
   size_t perm_hist;            /* int32          per-chunk expert histograms     */
+  size_t xq;                   /* uint8 [T, dim] MXFP8 codes of x (act_quant)   */
+  size_t xq_scales;            /* uint8 [T, dim/32] their E8M0 scales            */
+  size_t hq;                   /* uint8 [T*k, I] MXFP8 codes of H's routed rows  */
+  size_t hq_scales;            /* uint8 [T*k, I/32]                              */
   size_t h;                    /* [T*k + T, I]   SwiGLU activations (bf16/f32)   */
   size_t yrows;                /* [T*k + T, dim] weighted expert outputs         */
   int32_t max_tiles;

@@ -14,7 +14,7 @@ import torch  # loaded first so the library binds to the same HIP runtime as tor
 
 from dataclasses import replace
 
-from .config import DTYPE, LAYOUT, ROUTE, SCORE, MoEConfig
+from .config import ACT_QUANT, DTYPE, LAYOUT, ROUTE, SCORE, MoEConfig
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
@@ -45,6 +45,7 @@ class MoeConfigC(ctypes.Structure):
         ("swiglu_limit", ctypes.c_float), ("route_mode", ctypes.c_int32),
         ("vocab_size", ctypes.c_int64), ("act_dtype", ctypes.c_int32),
         ("expert_dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32),
+        ("act_quant", ctypes.c_int32),
     ]
 
 
@@ -58,7 +59,7 @@ class MoeWsLayoutC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total_bytes", "route_weights", "route_indices", "counts", "offsets", "sorted_tok",
         "sorted_slot", "sorted_weight", "inverse", "tiles", "tile_count", "flags",
-        "route_logits", "perm_hist", "h", "yrows")] + [
+        "route_logits", "perm_hist", "xq", "xq_scales", "hq", "hq_scales", "h", "yrows")] + [
         ("max_tiles", ctypes.c_int32), ("tile_rows", ctypes.c_int32)]
 
 
@@ -130,7 +131,8 @@ def config_c(cfg: MoEConfig) -> MoeConfigC:
         cfg.dim, cfg.n_routed_experts, cfg.n_activated_experts, cfg.n_expert_groups,
         cfg.n_limited_groups, cfg.moe_inter_dim, cfg.n_shared_experts, SCORE[cfg.score_func],
         cfg.route_scale, cfg.renormalize, cfg.swiglu_limit, ROUTE[cfg.route_mode],
-        cfg.vocab_size, DTYPE[cfg.act_dtype], DTYPE[cfg.expert_dtype], LAYOUT[cfg.weight_layout])
+        cfg.vocab_size, DTYPE[cfg.act_dtype], DTYPE[cfg.expert_dtype], LAYOUT[cfg.weight_layout],
+        ACT_QUANT[cfg.act_quant])
 
 
 def weights_c(layer: dict) -> MoeWeightsC:
@@ -309,7 +311,7 @@ def workspace_views(cfg: MoEConfig, T: int, ws):
         nbytes = n * torch.empty((), dtype=dtype).element_size()
         return ws[off:off + nbytes].view(dtype)
 
-    return {
+    out = {
         "route_weights": view(lay["route_weights"], T * k, torch.float32).view(T, k),
         "route_indices": view(lay["route_indices"], T * k, torch.int32).view(T, k),
         "counts": view(lay["counts"], E, torch.int32),
@@ -326,3 +328,10 @@ def workspace_views(cfg: MoEConfig, T: int, ws):
         "yrows": view(lay["yrows"], rows * cfg.dim, edt).view(rows, cfg.dim),
         "layout": lay,
     }
+    if cfg.act_quant == "mxfp8":
+        I = cfg.moe_inter_dim
+        out["xq"] = view(lay["xq"], T * cfg.dim, torch.uint8).view(T, cfg.dim)
+        out["xq_scales"] = view(lay["xq_scales"], T * cfg.dim // 32, torch.uint8).view(T, -1)
+        out["hq"] = view(lay["hq"], T * k * I, torch.uint8).view(T * k, I)
+        out["hq_scales"] = view(lay["hq_scales"], T * k * I // 32, torch.uint8).view(T * k, -1)
+    return out

@@ -11,6 +11,7 @@ SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
 ROUTE = {"learned": 0, "hash": 1, "ngram": 2}
 DTYPE = {"f32": 0, "bf16": 1, "fp4": 2}
 LAYOUT = {"rows": 0, "tiled": 1}
+ACT_QUANT = {"none": 0, "mxfp8": 1}
 
 
 @dataclass(frozen=True)
@@ -32,6 +33,7 @@ class MoEConfig:
     expert_dtype: str = "bf16"
     has_bias: bool = False
     weight_layout: str = "rows"   # expert matrices as given ("rows") or packed ("tiled")
+    act_quant: str = "none"       # FP4 routed experts: "mxfp8" activations on the scaled MFMA
 
     @property
     def renorm(self):
@@ -94,8 +96,13 @@ NGRAM_BF16 = Workload(
     description="2-gram hash routing (previous id, id) -> (a*q_j + b) mod 64, 8 sequences of 512 "
                 "Zipf(1.1) ids, d=2048, I=1024, bf16")
 
+V41_FLASH_FP4_MX = replace(
+    V41_FLASH_FP4, name="v41_flash_fp4_mx", cfg=replace(V41_FLASH_FP4.cfg, act_quant="mxfp8"),
+    description="V4.1-Flash shape with the routed FP4 experts on MXFP8 activations "
+                "(E4M3 + E8M0/32) and the scaled MFMA")
+
 FULL_WORKLOADS = {w.name: w for w in (TINY_FP32, HASH_BF16, V3_PREFILL, V3_DECODE, V41_FLASH_FP4,
-                                      NGRAM_BF16)}
+                                      NGRAM_BF16, V41_FLASH_FP4_MX)}
 
 # Reduced versions: the same structure at sizes the oracle finishes in
 # seconds while still spanning several GEMM tiles, slabs and a ragged tail.
@@ -126,6 +133,16 @@ SMALL_WORKLOADS = {
         "fp4_odd_widths",
         replace(V41_FLASH_FP4.cfg, dim=320, moe_inter_dim=192, n_routed_experts=48),
         T=77),
+    "fp4_mx_small": Workload(
+        "fp4_mx_small",
+        replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48,
+                act_quant="mxfp8"),
+        T=157, description="FP4 experts on MXFP8 activations (scaled MFMA)"),
+    "fp4_mx_clamp": Workload(
+        "fp4_mx_clamp",
+        replace(V41_FLASH_FP4.cfg, dim=384, moe_inter_dim=256, n_routed_experts=24,
+                act_quant="mxfp8"),
+        T=300, x_scale=20.0, description="MXFP8 activations with the clamp firing; 3 k-stages"),
     "fp4_clamp_small": Workload(
         "fp4_clamp_small",
         replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48),

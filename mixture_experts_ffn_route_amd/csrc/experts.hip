@@ -27,59 +27,9 @@
 // slabs of the same tiles), and the gathered rows of an expert stay in that
 // XCD's L2 while its slabs stream.
 
-#include "common.h"
-#include "internal.h"
+#include "gemm.h"
 
 namespace moe {
-
-struct GemmArgs {
-  const bf16 *A;             // activation rows [*, K]
-  const int32_t *a_rows;     // source row of each permuted row, or null (identity)
-  int K, N;
-  const void *B[2];          // routed weights [E, N, K] bf16 or FP4 bytes [E, N, K/2]
-  const uint8_t *S[2];       // FP4 scales [E, N, K/32]
-  const bf16 *SB[2];         // shared expert weights [N, K]
-  int E;                     // group id E = shared expert
-  bf16 *C;                   // output rows [*, N]
-  const int32_t *tiles, *tile_count;
-  int tile_begin, tile_end;  // tile_end < 0: end = *tile_count
-  int n_slabs;
-  float limit;               // SwiGLU clamp (two-matrix form); <= 0: none
-  const float *sorted_w;     // one-matrix form: gate value of each permuted row
-  int tiled;                 // B, S, SB in the tiled layout (moe_pack_weights)
-  float *Cf;                 // one-matrix form: fp32 output instead of C, or null
-  int n_shared_tiles;        // leading tiles of the range that are shared-expert tiles
-  int64_t dense_rows;        // tiles == null: one group of this many rows, cut
-  int dense_tile_rows;       //   into tiles of dense_tile_rows rows
-  int64_t routed_rows;       // T * k: rows at or above this belong to the shared expert
-};
-
-#define MOE_LDS __attribute__((address_space(3)))
-#define MOE_GLOBAL __attribute__((address_space(1)))
-
-// 16-byte asynchronous global -> LDS copy: lane l's 16 bytes land at
-// lds_block + 16*l (lds_block must be wave-uniform).  Completion is tracked by
-// vmcnt like any vector load.
-__device__ __forceinline__ void dma16(const void *gsrc, void *lds_block) {
-  __builtin_amdgcn_global_load_lds((MOE_GLOBAL void *)gsrc, (MOE_LDS void *)lds_block, 16, 0, 0);
-}
-
-// s_waitcnt immediate for vmcnt(n) (gfx9 encoding: vmcnt[3:0] in bits 3:0,
-// vmcnt[5:4] in bits 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima,
-// i.e. not waited on).
-#define MOE_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
-// Row blocks are processed in chunks of MCH (a tile's block count is rounded
-// up to a multiple of MCH): every pipeline stage is then straight-line code
-// in which the LDS reads of a chunk issue back to back and the MFMAs of one
-// chunk overlap the reads of the next.  Padding blocks read real rows (the
-// tile's last row) and are never stored.
-constexpr int MCH = 4;
-
-struct TileCtx {
-  int grp, row0, rows, col0, lane, wave, K, N;
-  bool shared;
-};
 
 // One tile: MBE row blocks (compile time), NB weight matrices (2: gate|up
 // with the SwiGLU epilogue, 1: down with the gate-value epilogue), NCB
@@ -374,51 +324,9 @@ void grouped_gemm(const GemmArgs g) {
   constexpr int SLOT = gemm_slot_elems<WAVES, NB, NCB, MB, FP4, NS>();
   __shared__ __attribute__((aligned(1024))) bf16 As[NS * SLOT];
 
-  // ---- work item (XCD-aware).  Workgroups are dealt round-robin to the 8
-  // XCDs (blockIdx & 7).  Shared-expert tiles (every one a full, compute-heavy
-  // tile whose weights all XCDs would otherwise wait on) go to the XCDs in
-  // turn, all slabs of a tile on one XCD; the routed items are then split
-  // into 8 contiguous runs, so an expert's slabs share one XCD's L2. ----
-  const int tend = g.tile_end >= 0 ? g.tile_end : *g.tile_count;
-  const int nsh = g.n_shared_tiles;
-  const int xcd = blockIdx.x & 7;
-  const int64_t slot = blockIdx.x >> 3;
-  const int sh_cnt = nsh > xcd ? (nsh - xcd + 7) >> 3 : 0;
-  const int64_t sh_items = (int64_t)sh_cnt * g.n_slabs;
   int tile, slab;
-  if (slot < sh_items) {
-    const int i = (int)(slot / g.n_slabs);
-    tile = g.tile_begin + xcd + 8 * i;
-    slab = (int)(slot - (int64_t)i * g.n_slabs);
-  } else {
-    const int64_t routed = (int64_t)(tend - g.tile_begin - nsh) * g.n_slabs;
-    const int64_t r_per = (routed + 7) >> 3;
-    const int64_t r = slot - sh_items;
-    if (r >= r_per) return;
-    const int64_t item = xcd * r_per + r;
-    if (item >= routed) return;
-    const int64_t rt = item / g.n_slabs;
-    tile = g.tile_begin + nsh + (int)rt;
-    slab = (int)(item - rt * g.n_slabs);
-  }
-
-  TileCtx t;
-  if (g.tiles) {
-    t.grp = g.tiles[4 * tile];
-    t.row0 = g.tiles[4 * tile + 1];
-    t.rows = g.tiles[4 * tile + 2];
-  } else {
-    t.grp = 0;
-    t.row0 = tile * g.dense_tile_rows;
-    const int64_t left = g.dense_rows - t.row0;
-    t.rows = left < g.dense_tile_rows ? (int)left : g.dense_tile_rows;
-  }
-  t.shared = t.grp == g.E;
-  t.K = g.K;
-  t.N = g.N;
-  t.lane = threadIdx.x & 63;
-  t.wave = threadIdx.x >> 6;
-  t.col0 = slab * (WAVES * NCB * 16) + t.wave * NCB * 16;
+  if (!gemm_work_item(g, &tile, &slab)) return;
+  const TileCtx t = gemm_tile_ctx(g, tile, slab, WAVES, NCB * 16);
   const int nmb = (t.rows + 15) >> 4;
 
   if constexpr (MB < MCH) {
@@ -576,10 +484,7 @@ static hipError_t run_gemm(const GemmArgs &a, int max_tiles, hipStream_t s) {
   if constexpr (!gemm_cfg_fits<WAVES, NB, NCB, MB, FP4, NS>()) {
     return hipErrorInvalidValue;
   } else {
-  // per XCD: its share of the shared tiles, then an eighth of the rest
-  const int64_t per_xcd = (int64_t)((a.n_shared_tiles + 7) / 8) * a.n_slabs +
-                          ((int64_t)(max_tiles - a.n_shared_tiles) * a.n_slabs + 7) / 8;
-  const int64_t blocks = 8 * per_xcd;
+  const int64_t blocks = gemm_grid_blocks(a, max_tiles);
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((grouped_gemm<WAVES, NB, NCB, MB, FP4, NS>), dim3((unsigned)blocks),
                      dim3(WAVES * 64), 0, s, a);
@@ -718,8 +623,19 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
       if ((err = gemm_launch(2, false, mb, sh, p.n_shared_tiles, s)) != hipSuccess) return err;
     }
     a.tile_begin = p.n_shared_tiles; a.tile_end = -1;
-    if ((err = gemm_launch(2, true, mb, a, p.max_tiles - p.n_shared_tiles, s)) != hipSuccess)
+    if (p.mx) {
+      // routed experts on MXFP8 activations: quantise x, gather its rows
+      if ((err = launch_quantize_mxfp8((const bf16 *)p.x, p.T, p.dim, p.xq, p.xq_scales, s)) !=
+          hipSuccess)
+        return err;
+      a.Aq = p.xq;
+      a.Asc = p.xq_scales;
+      if ((err = launch_gemm_mx(2, mb, a, p.max_tiles - p.n_shared_tiles, s)) != hipSuccess)
+        return err;
+    } else if ((err = gemm_launch(2, true, mb, a, p.max_tiles - p.n_shared_tiles, s)) !=
+               hipSuccess) {
       return err;
+    }
   } else {
     a.tile_begin = 0; a.tile_end = -1;
     a.n_shared_tiles = p.n_shared_tiles;
@@ -743,8 +659,19 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
       if ((err = gemm_launch(1, false, mb, sh, p.n_shared_tiles, s)) != hipSuccess) return err;
     }
     a.tile_begin = p.n_shared_tiles; a.tile_end = -1;
-    if ((err = gemm_launch(1, true, mb, a, p.max_tiles - p.n_shared_tiles, s)) != hipSuccess)
+    if (p.mx) {
+      // the routed rows of H (the first T*k) in MXFP8, in permuted order
+      if ((err = launch_quantize_mxfp8((const bf16 *)p.h, routed_rows, p.inter, p.hq,
+                                       p.hq_scales, s)) != hipSuccess)
+        return err;
+      a.Aq = p.hq;
+      a.Asc = p.hq_scales;
+      if ((err = launch_gemm_mx(1, mb, a, p.max_tiles - p.n_shared_tiles, s)) != hipSuccess)
+        return err;
+    } else if ((err = gemm_launch(1, true, mb, a, p.max_tiles - p.n_shared_tiles, s)) !=
+               hipSuccess) {
       return err;
+    }
   } else {
     a.tile_begin = 0; a.tile_end = -1;
     a.n_shared_tiles = p.n_shared_tiles;

@@ -68,6 +68,8 @@ struct ExpertPlan {
   float swiglu_limit;
   int act_dtype, expert_dtype;
   bool tiled;            // expert matrices in MOE_LAYOUT_TILED
+  bool mx;               // FP4 routed experts on MXFP8 activations
+  uint8_t *xq, *xq_scales, *hq, *hq_scales;   // MXFP8 copies of x and of H's routed rows
   const void *x;
   const moe_weights *w;
   const float *route_w;

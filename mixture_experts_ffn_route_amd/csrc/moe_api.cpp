@@ -52,6 +52,12 @@ int validate(const moe_config *c) {
     return MOE_ERR_INVALID_ARG;
   if (c->weight_layout == MOE_LAYOUT_TILED && c->act_dtype != MOE_DTYPE_BF16)
     return MOE_ERR_UNSUPPORTED;
+  if (c->act_quant != MOE_ACT_QUANT_NONE && c->act_quant != MOE_ACT_QUANT_MXFP8)
+    return MOE_ERR_INVALID_ARG;
+  if (c->act_quant == MOE_ACT_QUANT_MXFP8) {
+    if (c->expert_dtype != MOE_DTYPE_FP4_E2M1) return MOE_ERR_INVALID_ARG;
+    if (c->dim % 128 != 0 || c->moe_inter_dim % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  }
   if (k > 16 || E > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->route_mode == MOE_ROUTE_HASH) {
     if (c->vocab_size < 1) return MOE_ERR_INVALID_ARG;
@@ -101,6 +107,11 @@ int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
   l.flags = take(sizeof(uint32_t) * 4);
   l.route_logits = take(sizeof(float) * moe::route_logits_floats(*c, T));
   l.perm_hist = take(sizeof(int32_t) * moe::permute_chunks(T * k) * E);
+  const bool mx = c->act_quant == MOE_ACT_QUANT_MXFP8;
+  l.xq = take(mx ? (size_t)T * c->dim : 0);
+  l.xq_scales = take(mx ? (size_t)T * c->dim / 32 : 0);
+  l.hq = take(mx ? (size_t)T * k * c->moe_inter_dim : 0);
+  l.hq_scales = take(mx ? (size_t)T * k * c->moe_inter_dim / 32 : 0);
   l.h = take(es * rows * c->moe_inter_dim);
   l.yrows = take(es * rows * c->dim);
   l.total_bytes = off;
@@ -378,6 +389,11 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   p.act_dtype = cfg->act_dtype;
   p.expert_dtype = cfg->expert_dtype;
   p.tiled = cfg->weight_layout == MOE_LAYOUT_TILED;
+  p.mx = cfg->act_quant == MOE_ACT_QUANT_MXFP8;
+  p.xq = (uint8_t *)(base + L.xq);
+  p.xq_scales = (uint8_t *)(base + L.xq_scales);
+  p.hq = (uint8_t *)(base + L.hq);
+  p.hq_scales = (uint8_t *)(base + L.hq_scales);
   p.x = x;
   p.w = w;
   p.route_w = route_w;

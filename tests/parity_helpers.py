@@ -108,6 +108,14 @@ def compare_routing(cfg, gpu_w, gpu_idx, ora_w, ora_idx, aux):
     return differ
 
 
+def oracle_forward(cfg, x, weights, indices, layer):
+    """The oracle layer for cfg: bf16 activations, or MXFP8 activations on the
+    routed FP4 experts."""
+    f = oracle.layer_forward_mx if cfg.act_quant == "mxfp8" else oracle.layer_forward
+    return f(x, weights, indices, expert_fetcher(layer, cfg), shared_weights(layer, cfg),
+             cfg.swiglu_limit)
+
+
 def max_rel_err(y, ref):
     denom = np.max(np.abs(ref))
     return float(np.max(np.abs(y - ref)) / denom) if denom > 0 else float(np.max(np.abs(y)))

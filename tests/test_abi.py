@@ -68,6 +68,9 @@ BAD = [
     ("learned E > 512", replace(V3, n_routed_experts=1024, n_expert_groups=1, n_limited_groups=1), B.MOE_ERR_UNSUPPORTED),
     ("group lanes not a power of two", replace(V3, n_routed_experts=96, n_expert_groups=8, n_limited_groups=4), B.MOE_ERR_UNSUPPORTED),
     ("tiled fp32 layer", replace(C.TINY_FP32.cfg, weight_layout="tiled"), B.MOE_ERR_UNSUPPORTED),
+    ("mxfp8 on bf16 experts", replace(V3, act_quant="mxfp8"), B.MOE_ERR_INVALID_ARG),
+    ("mxfp8 dim % 128", replace(C.V41_FLASH_FP4_MX.cfg, dim=5120 + 64), B.MOE_ERR_UNSUPPORTED),
+    ("mxfp8 inter % 128", replace(C.V41_FLASH_FP4_MX.cfg, moe_inter_dim=1536 + 64), B.MOE_ERR_UNSUPPORTED),
 ]
 
 
@@ -87,6 +90,9 @@ def test_enum_range_checked():
     assert B._lib.moe_validate_config(None) == B.MOE_ERR_INVALID_ARG
     c = B.config_c(V3)
     c.weight_layout = 2
+    assert B._lib.moe_validate_config(ctypes.byref(c)) == B.MOE_ERR_INVALID_ARG
+    c = B.config_c(C.V41_FLASH_FP4.cfg)
+    c.act_quant = 2
     assert B._lib.moe_validate_config(ctypes.byref(c)) == B.MOE_ERR_INVALID_ARG
     assert B.moe_validate_config(replace(V3, weight_layout="tiled")) == B.MOE_OK
 

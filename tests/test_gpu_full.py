@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 # tokens whose output the oracle recomputes (None: all of them)
 SAMPLE = {"tiny_fp32": None, "v3_decode": None, "hash_bf16": 64, "v3_prefill": 24,
-          "v41_flash_fp4": 16, "ngram_bf16": 64}
+          "v41_flash_fp4": 16, "ngram_bf16": 64, "v41_flash_fp4_mx": 16}
 
 
 def _sample_rows(T, n, seed):
@@ -94,8 +94,7 @@ def test_forward_full_size(name, gpu):
     rows = rows[~differ[rows]]
     print(f"[full] {name}: oracle forward of {rows.size} tokens", flush=True)
     x_rows = H.f64(layer["x"][torch.as_tensor(rows, device=gpu)])
-    yref = oracle.layer_forward(x_rows, ow[rows], oidx[rows], H.expert_fetcher(layer, cfg),
-                                H.shared_weights(layer, cfg), cfg.swiglu_limit)
+    yref = H.oracle_forward(cfg, x_rows, ow[rows], oidx[rows], layer)
     ygpu = H.f64(y[torch.as_tensor(rows, device=gpu)])
     err = H.max_rel_err(ygpu, yref)
     tol = H.TOL[cfg.expert_dtype if cfg.expert_dtype == "fp4" else cfg.act_dtype]

@@ -133,13 +133,27 @@ def test_forward_small(name, gpu):
         np.testing.assert_array_equal(st[:T * cfg.n_activated_experts], ost)
         np.testing.assert_array_equal(inv, oinv)
     keep = ~differ
-    yref = oracle.layer_forward(H.f64(layer["x"])[keep], ow[keep], oidx[keep],
-                                H.expert_fetcher(layer, cfg), H.shared_weights(layer, cfg),
-                                cfg.swiglu_limit)
+    yref = H.oracle_forward(cfg, H.f64(layer["x"])[keep], ow[keep], oidx[keep], layer)
     err = H.max_rel_err(H.f64(y)[keep], yref)
     print(f"[forward] {name}: max rel err {err:.3e}", flush=True)
     assert err <= H.TOL[cfg.expert_dtype if cfg.expert_dtype == "fp4" else cfg.act_dtype]
     assert int(v["flags"][0]) == 0
+
+
+@pytest.mark.parametrize("name", [n for n, w in C.SMALL_WORKLOADS.items()
+                                  if w.cfg.act_quant == "mxfp8"])
+def test_mxfp8_activation_codes(name, gpu):
+    """The workspace keeps x quantised to MXFP8.  x is the synthetic input, so
+    its E4M3 codes and E8M0 shared exponents must equal the oracle's bit for
+    bit (both sides scale by a power of two and round to nearest even)."""
+    wl = C.SMALL_WORKLOADS[name]
+    cfg, T = wl.cfg, wl.T
+    layer, _ = _layer(wl, gpu)
+    _, ws = _forward(wl, layer, gpu)
+    v = B.workspace_views(cfg, T, ws)
+    codes, scales = oracle.mxfp8_quantize(H.f64(layer["x"]))
+    np.testing.assert_array_equal(H.cpu_np(v["xq_scales"]), scales)
+    np.testing.assert_array_equal(H.cpu_np(v["xq"]), codes)
 
 
 def test_forward_deterministic(gpu):
