@@ -138,6 +138,11 @@ SMALL_WORKLOADS = {
         replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48,
                 act_quant="mxfp8"),
         T=157, description="FP4 experts on MXFP8 activations (scaled MFMA)"),
+    "fp4_mx_decode": Workload(
+        "fp4_mx_decode",
+        replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=256, n_routed_experts=48,
+                act_quant="mxfp8"),
+        T=9, description="MXFP8 activations, decode batch: one-row-block tiles"),
     "fp4_mx_clamp": Workload(
         "fp4_mx_clamp",
         replace(V41_FLASH_FP4.cfg, dim=384, moe_inter_dim=256, n_routed_experts=24,

@@ -464,9 +464,12 @@ int choose_tile_rows(const moe_config &cfg, int64_t T) {
   if (cfg.act_dtype == MOE_DTYPE_F32) return 16;
   const double avg = (double)T * cfg.n_activated_experts / cfg.n_routed_experts;
   const double want = avg + 3.0 * sqrt(avg) + 4.0;
+  // MXFP8 tiles stop at 12 row blocks: the row-split kernel then holds a
+  // 128-column slab of each matrix in registers
+  const int cap = cfg.act_quant == MOE_ACT_QUANT_MXFP8 ? 192 : 256;
   for (int mb : kTileMB)
-    if (16.0 * mb >= want) return 16 * mb;
-  return 256;
+    if (16.0 * mb >= want) return 16 * mb < cap ? 16 * mb : cap;
+  return cap;
 }
 
 // Whether a configuration fits the hardware: the in-flight vector memory ops

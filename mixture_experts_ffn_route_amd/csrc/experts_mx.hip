@@ -305,6 +305,349 @@ __device__ __forceinline__ void gemm_tile_mx(const GemmArgs &g, const TileCtx &t
   }
 }
 
+constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+// LDS of the row-split kernel: NSA activation slots and NSB weight slots,
+// each its own object so the compiler can tell copies into one slot from
+// reads of another (and adds no waits between them).
+struct MxRing {
+  uint8_t *a[4];
+  uint8_t *b[8];
+};
+
+// Row-split tile for tiles of 4 and more row blocks.  Each wave owns MW =
+// MBE/WAVES row blocks and every column of the slab: SC 16-column blocks of
+// each of the NB matrices.  Per stage of 128 inputs each wave copies its own
+// activation rows into LDS (full 128-byte lines, 8 rows per copy, the 16-byte
+// chunk of lane l at (l%8) ^ (l/8) so the reads are conflict-free) and reads
+// them back once; the FP4 weight fragments (16 columns x 128 inputs, 1 KB)
+// and the scales are copied once per workgroup and read by every wave.  So
+// an activation byte crosses LDS once, not once per column wave.
+//
+// Two copy rings: activations (from L2) NSA stages deep, weights (streamed
+// from HBM) NSB stages deep.  Each stage issues its activation copies first
+// and its weight copies last: the in-order count then lets the wait for a
+// stage's activations leave the far weight copies in flight.
+//
+// LDS form of a weight fragment.  Tiled weights: the 16-byte chunk (t, g, p)
+// of the stage (64-input tile t, 8-byte group g, column pair p) is stored at
+// chunk t*32 + (g%2)*16 + (g/2)*8 + p, so the two 8-byte pieces a lane needs
+// sit 256 bytes apart and 32 lanes of a read touch all 64 banks once.  Row
+// weights: chunk (column r, 32-input part c) at chunk 16c + r, the lane's 16
+// bytes contiguous.  Weight scales: the 64 bytes of the stage in the global
+// order (tiled: [tile][column][block%2], rows: [column][block]).
+template <int WAVES, int NB, int SC, int MBE, int NSA, int NSB, int A_MAX>
+__device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx &t,
+                                                const MxRing &ring) {
+  constexpr int BK = 128;
+  constexpr int MW = MBE / WAVES;                  // row blocks of one wave
+  constexpr int NFR = NB * SC;                     // weight fragments per stage
+  constexpr int NBU = (NFR + WAVES - 1) / WAVES;   // fragment copies per wave
+  constexpr int NSG = (NFR + 3) / 4;               // weight-scale copies (4 fragments each)
+  constexpr int NSU = (NSG + WAVES - 1) / WAVES;   // per wave
+  constexpr int AS_OFF = A_MAX * 2 * 1024;         // activation slot: units, then scales
+  constexpr int S_OFF = NBU * WAVES * 1024;        // weight slot: fragments, then scales
+  constexpr int VMA = 2 * MW + 1;                  // activation copies per stage
+  constexpr int VMB = NBU + NSU;                   // weight copies per stage
+  constexpr int VM = VMA + VMB;
+  // copies issued after the last one a stage needs: its activations (first in
+  // their issuing stage) when the weight ring is deeper, else its weights
+  constexpr int WAIT = (NSB > NSA ? VMB : 0) + (NSA - 2) * VM;
+  constexpr int GROUP = NSA * NSB / gcd_int(NSA, NSB);
+  constexpr int ISSUE_PER_FRAG = (VM + NFR - 1) / NFR;
+  static_assert(MBE % WAVES == 0 && MBE <= A_MAX, "row blocks split evenly over the waves");
+  static_assert(MW * 16 <= 64, "one activation-scale copy per wave");
+  static_assert(NSA >= 2 && NSA <= 4 && NSB >= NSA && NSB <= 8, "ring depths");
+  static_assert(WAIT <= 63, "vmcnt holds 6 bits");
+
+  const int lane = t.lane, wave = t.wave, r16 = lane & 15, q = lane >> 4;
+  const int K = t.K, N = t.N, rows = t.rows, row0 = t.row0, col0 = t.col0;
+  const int KS = K / 32;
+  const int mb0 = wave * MW;
+  const bool tiled = g.tiled != 0;
+
+  float row_w[NB == 1 ? MW : 1][4];
+  if constexpr (NB == 1) {
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int r = (mb0 + m) * 16 + q * 4 + i;
+        r = r < rows ? r : rows - 1;
+        const int64_t R = row0 + r;
+        row_w[m][i] = R < g.routed_rows ? g.sorted_w[R < g.routed_rows ? R : 0] : 1.f;
+      }
+  }
+
+  // activation copies of this wave: unit (m, h) = rows 16(mb0+m) + 8h .. +7
+  const uint8_t *asrc[MW][2];
+#pragma unroll
+  for (int m = 0; m < MW; ++m)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int r = (mb0 + m) * 16 + h * 8 + (lane >> 3);
+      r = r < rows ? r : rows - 1;
+      const int64_t src = g.a_rows ? g.a_rows[row0 + r] : (int64_t)(row0 + r);
+      asrc[m][h] = g.Aq + src * K + 16 * ((lane & 7) ^ (lane >> 3));
+    }
+  // activation-scale copy: lane l fetches the stage's 4 scale bytes of row
+  // 16*mb0 + l (lanes past the wave's rows repeat its last row)
+  const uint8_t *assrc;
+  {
+    int r = mb0 * 16 + (lane < MW * 16 ? lane : MW * 16 - 1);
+    r = r < rows ? r : rows - 1;
+    const int64_t src = g.a_rows ? g.a_rows[row0 + r] : (int64_t)(row0 + r);
+    assrc = g.Asc + src * KS;
+  }
+  // weight copies: unit u = wave + WAVES*i is fragment (u / SC, u % SC)
+  const int64_t bst = tiled ? 1024 : 64;
+  const int64_t sst = tiled ? 64 : 4;
+  const uint8_t *bsrc[NBU];
+#pragma unroll
+  for (int i = 0; i < NBU; ++i) {
+    const int u0 = wave + WAVES * i;
+    const int u = u0 < NFR ? u0 : 0;
+    const int b = u / SC, cb = u - b * SC;
+    const int64_t nb = (col0 >> 4) + cb;
+    const uint8_t *mat = (const uint8_t *)g.B[b] + (int64_t)t.grp * N * (K / 2);
+    if (tiled) {
+      const int tt = lane >> 5, gg = ((lane >> 3) & 1) * 2 + ((lane >> 4) & 1), pp = lane & 7;
+      bsrc[i] = mat + nb * (K / 64) * 512 + tt * 512 + gg * 128 + pp * 16;
+    } else {
+      bsrc[i] = mat + (nb * 16 + (lane & 15)) * (K / 2) + 16 * (lane >> 4);
+    }
+  }
+  const uint8_t *ssrc[NSU];
+#pragma unroll
+  for (int i = 0; i < NSU; ++i) {
+    const int j0 = wave + WAVES * i;
+    const int j = j0 < NSG ? j0 : 0;
+    const int f0 = j * 4 + (lane >> 4);
+    const int f = f0 < NFR ? f0 : 0;
+    const int b = f / SC, cb = f - b * SC;
+    const int64_t nb = (col0 >> 4) + cb;
+    const uint8_t *smat = g.S[b] + (int64_t)t.grp * N * KS;
+    ssrc[i] = tiled ? smat + nb * (K / 64) * 32 + 4 * (lane & 15)
+                    : smat + (nb * 16 + (lane & 15)) * KS;
+  }
+  // this lane's reads: activation chunks q and 4+q of row r16 of a row block,
+  // its scale byte, a weight fragment's two 8-byte pieces and scale byte
+  const int rr = r16 & 7;
+  const int a_lo = (r16 >> 3) * 1024 + (rr * 8 + (q ^ rr)) * 16;
+  const int a_hi = (r16 >> 3) * 1024 + (rr * 8 + ((4 + q) ^ rr)) * 16;
+  const int a_sc = AS_OFF + wave * 256 + r16 * 4 + q;
+  const int boff0 = tiled ? ((q >> 1) * 32 + (q & 1) * 8 + (r16 >> 1)) * 16 + (r16 & 1) * 8
+                          : (q * 16 + r16) * 16;
+  const int boff1 = boff0 + (tiled ? 256 : 8);
+  const int soff = S_OFF + (tiled ? (q >> 1) * 32 + r16 * 2 + (q & 1) : r16 * 4 + q);
+
+  f32x4 acc[MW][NB][SC];
+#pragma unroll
+  for (int m = 0; m < MW; ++m)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int cb = 0; cb < SC; ++cb) acc[m][b][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nst = K / BK;
+  const int last = nst - 1;
+  // copy qq of a stage: activations of stage STA into slot SA (qq < VMA),
+  // then weights of stage STB into slot SB
+  auto issue_op = [&](int SA, int STA, int SB, int STB, int qq) {
+    if (qq < 2 * MW) {
+      const int m = qq >> 1, h = qq & 1;
+      dma16(asrc[m][h] + (int64_t)STA * BK, ring.a[SA] + ((mb0 + m) * 2 + h) * 1024);
+    } else if (qq == 2 * MW) {
+      dma4(assrc + 4 * STA, ring.a[SA] + AS_OFF + wave * 256);
+    } else if (qq < VMA + NBU) {
+      const int i = qq - VMA;
+      dma16(bsrc[i] + STB * bst, ring.b[SB] + (wave + WAVES * i) * 1024);
+    } else {
+      const int i = qq - VMA - NBU;
+      dma4(ssrc[i] + STB * sst, ring.b[SB] + S_OFF + (wave + WAVES * i) * 256);
+    }
+  };
+  // prologue: virtual stages -(NSB-1) .. -1 issue what the steady state would
+  // (weights of stage s+NSB-1, activations of stage s+NSA-1 once s >= 1-NSA)
+#pragma unroll
+  for (int v = 0; v < NSB - 1; ++v) {
+    const int sb = v, sa = v - (NSB - NSA);
+    const int stb = sb < last ? sb : last;
+    if (sa >= 0) {
+      const int sta = sa < last ? sa : last;
+#pragma unroll
+      for (int qq = 0; qq < VMA; ++qq) issue_op(sa % NSA, sta, 0, 0, qq);
+    }
+#pragma unroll
+    for (int qq = VMA; qq < VM; ++qq) issue_op(0, 0, sb % NSB, stb, qq);
+  }
+
+  // stage with activations in slot pa and weights in slot pb; refills
+  // activations of stage nxa into slot (pa+NSA-1)%NSA and weights of stage nxb
+  // into slot (pb+NSB-1)%NSB, interleaved with the MFMAs
+  auto compute_stage = [&](int pa, int pb, int nxa, int nxb) {
+    const int na = (pa + NSA - 1) % NSA, nb = (pb + NSB - 1) % NSB;
+    const uint8_t *aslot = ring.a[pa];
+    const uint8_t *bslot = ring.b[pb];
+    i32x8 av[MW];
+    int sa[MW];
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+      const uint8_t *u = aslot + (mb0 + m) * 2048;
+      const u32x4 lo = *(const u32x4 *)(u + a_lo);
+      const u32x4 hi = *(const u32x4 *)(u + a_hi);
+      av[m] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      sa[m] = aslot[a_sc + m * 64];
+    }
+    // weight fragments are read one ahead of their MFMAs
+    i32x8 bv[2];
+    int sbv[2];
+    auto read_frag = [&](int f, int buf) {
+      const uint2 lo = *(const uint2 *)(bslot + f * 1024 + boff0);
+      const uint2 hi = *(const uint2 *)(bslot + f * 1024 + boff1);
+      bv[buf] = i32x8{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y, 0, 0, 0, 0};
+      sbv[buf] = bslot[soff + f * 64];
+    };
+    read_frag(0, 0);
+#pragma unroll
+    for (int f = 0; f < NFR; ++f) {
+      if (f + 1 < NFR) read_frag(f + 1, (f + 1) & 1);
+      const int b = f / SC, cb = f - b * SC;
+#pragma unroll
+      for (int m = 0; m < MW; ++m)
+        acc[m][b][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            av[m], bv[f & 1], acc[m][b][cb], 0, 4, 0, sa[m], 0, sbv[f & 1]);
+#pragma unroll
+      for (int j = 0; j < ISSUE_PER_FRAG; ++j) {
+        const int qq = f * ISSUE_PER_FRAG + j;
+        if (qq < VM) issue_op(na, nxa, nb, nxb, qq);
+      }
+    }
+  };
+
+  // whole groups of GROUP stages (a multiple of both ring depths): no branch
+  // inside, a fixed number of copies in flight (stages past the end re-copy
+  // the last one)
+  const int nfull = nst - nst % GROUP;
+  for (int s0 = 0; s0 < nfull; s0 += GROUP) {
+#pragma unroll
+    for (int p = 0; p < GROUP; ++p) {
+      const int st = s0 + p;
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT(WAIT));
+      __builtin_amdgcn_s_barrier();
+      compute_stage(p % NSA, p % NSB, st + NSA - 1 < last ? st + NSA - 1 : last,
+                    st + NSB - 1 < last ? st + NSB - 1 : last);
+    }
+  }
+  // the last nst % GROUP stages, with full waits (they still refill, since a
+  // stage's copies are issued NSA-1 / NSB-1 stages ahead)
+#pragma unroll
+  for (int p = 0; p < GROUP - 1; ++p) {
+    const int st = nfull + p;
+    if (st < nst) {
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+      __builtin_amdgcn_s_barrier();
+      compute_stage(p % NSA, p % NSB, st + NSA - 1 < last ? st + NSA - 1 : last,
+                    st + NSB - 1 < last ? st + NSB - 1 : last);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+
+  if constexpr (NB == 2) {
+    const float L = g.limit;
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (mb0 + m) * 16 + q * 4 + i;
+        if (row < rows) {
+          bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
+#pragma unroll
+          for (int cb = 0; cb < SC; ++cb) {
+            float gv = acc[m][0][cb][i], uv = acc[m][1][cb][i];
+            if (L > 0.f) {
+              gv = fminf(gv, L);
+              uv = fminf(fmaxf(uv, -L), L);
+            }
+            crow[cb * 16] = (bf16)(gv / (1.f + __expf(-gv)) * uv);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (mb0 + m) * 16 + q * 4 + i;
+        if (row < rows) {
+          bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
+#pragma unroll
+          for (int cb = 0; cb < SC; ++cb) crow[cb * 16] = (bf16)(acc[m][0][cb][i] * row_w[m][i]);
+        }
+      }
+  }
+}
+
+template <int WAVES, int MB>
+constexpr int gemm_mx_rs_aslot_bytes() { return MB * 2 * 1024 + WAVES * 256; }
+
+template <int WAVES, int NB, int SC>
+constexpr int gemm_mx_rs_bslot_bytes() {
+  constexpr int NFR = NB * SC;
+  constexpr int NBU = (NFR + WAVES - 1) / WAVES;
+  constexpr int NSU = ((NFR + 3) / 4 + WAVES - 1) / WAVES;
+  return NBU * WAVES * 1024 + NSU * WAVES * 256;
+}
+
+// Row-split kernel: the tile height is taken as the smallest multiple of
+// WAVES row blocks (and of 4) that holds the tile's rows, up to MB.
+template <int WAVES, int NB, int SC, int MB, int NSA, int NSB, int WPE>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void grouped_gemm_mx_rs(const GemmArgs g) {
+  constexpr int SA = gemm_mx_rs_aslot_bytes<WAVES, MB>();
+  constexpr int SB = gemm_mx_rs_bslot_bytes<WAVES, NB, SC>();
+  constexpr int STEP = WAVES > 4 ? WAVES : 4;
+  static_assert(MB % STEP == 0, "tile height in whole steps");
+  __shared__ __attribute__((aligned(1024))) uint8_t A0[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t A1[SA];
+  __shared__ __attribute__((aligned(1024))) uint8_t A2[NSA > 2 ? SA : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t A3[NSA > 3 ? SA : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t B0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t B1[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t B2[NSB > 2 ? SB : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t B3[NSB > 3 ? SB : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t B4[NSB > 4 ? SB : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t B5[NSB > 5 ? SB : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t B6[NSB > 6 ? SB : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t B7[NSB > 7 ? SB : 1];
+  const MxRing ring{{A0, A1, A2, A3}, {B0, B1, B2, B3, B4, B5, B6, B7}};
+  int tile, slab;
+  if (!gemm_work_item(g, &tile, &slab)) return;
+  TileCtx t = gemm_tile_ctx(g, tile, slab, 1, SC * 16);
+  t.col0 = slab * (SC * 16);                // every wave covers the whole slab
+  const int nmb = (t.rows + 15) >> 4;
+  if (MB <= STEP || nmb <= STEP)
+    gemm_tile_mx_rs<WAVES, NB, SC, STEP, NSA, NSB, MB>(g, t, ring);
+  else if (MB <= 2 * STEP || nmb <= 2 * STEP)
+    gemm_tile_mx_rs<WAVES, NB, SC, (MB < 2 * STEP ? MB : 2 * STEP), NSA, NSB, MB>(g, t, ring);
+  else if (MB <= 3 * STEP || nmb <= 3 * STEP)
+    gemm_tile_mx_rs<WAVES, NB, SC, (MB < 3 * STEP ? MB : 3 * STEP), NSA, NSB, MB>(g, t, ring);
+  else
+    gemm_tile_mx_rs<WAVES, NB, SC, MB, NSA, NSB, MB>(g, t, ring);
+}
+
+template <int WAVES, int NB, int SC, int MB, int NSA, int NSB, int WPE>
+hipError_t run_gemm_mx_rs(GemmArgs a, int max_tiles, hipStream_t s) {
+  if (a.N % (SC * 16)) return hipErrorInvalidValue;
+  a.n_slabs = a.N / (SC * 16);
+  const int64_t blocks = gemm_grid_blocks(a, max_tiles);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_mx_rs<WAVES, NB, SC, MB, NSA, NSB, WPE>),
+                     dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int WAVES, int NB, int NCB, int MB, int NS>
 constexpr int gemm_mx_slot_bytes() {
   constexpr int NFW = (MB * 2 + WAVES - 1) / WAVES;
@@ -348,17 +691,23 @@ hipError_t run_gemm_mx(GemmArgs a, int max_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Short tiles: 8 waves, two per SIMD; tiles of 12+ row blocks: 4 waves with
-// the whole register file.  Column blocks per wave: 1 for gate|up, 2 for down
-// when the width allows (else 1).
+// Decode tiles (one row block): 8 waves splitting the columns.  Tiles of 4+
+// row blocks: the row-split kernel, 4 waves with the whole register file.
+// Every slab re-reads the tile's activations, so the slabs are as wide as the
+// accumulators allow: for tiles of up to 12 row blocks 128 columns of gate and
+// of up, or 256 down columns (half that when the width does not divide).
 template <int NB, int MB>
 hipError_t run_gemm_mx_mb(GemmArgs a, int max_tiles, hipStream_t s) {
-  constexpr bool tall = MB >= 12;
-  constexpr int W = tall ? 4 : 8;
-  constexpr int WPE = tall ? 1 : 2;
-  if (NB == 1 && a.N % (W * 32) == 0) return run_gemm_mx<W, 1, 2, MB, 3, WPE>(a, max_tiles, s);
-  if (a.N % (W * 16) == 0) return run_gemm_mx<W, NB, 1, MB, 3, WPE>(a, max_tiles, s);
-  return run_gemm_mx<4, NB, 1, MB, 3, 1>(a, max_tiles, s);     // N % 64 == 0
+  if constexpr (MB >= 4) {
+    constexpr int NARROW = NB == 2 ? 4 : 8;
+    constexpr int WIDE = MB <= 12 ? 2 * NARROW : NARROW;
+    if (a.N % (WIDE * 16) == 0) return run_gemm_mx_rs<4, NB, WIDE, MB, 3, 3, 1>(a, max_tiles, s);
+    return run_gemm_mx_rs<4, NB, NARROW, MB, 3, 3, 1>(a, max_tiles, s);
+  } else {
+    if (NB == 1 && a.N % 256 == 0) return run_gemm_mx<8, 1, 2, MB, 3, 2>(a, max_tiles, s);
+    if (a.N % 128 == 0) return run_gemm_mx<8, NB, 1, MB, 3, 2>(a, max_tiles, s);
+    return run_gemm_mx<4, NB, 1, MB, 3, 1>(a, max_tiles, s);     // N % 64 == 0
+  }
 }
 
 template <int NB>
