@@ -26,17 +26,38 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at V3 shape (T=4096 prefill, T=64 decode) + % MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp4": 2500.0, "f32": 157.3}   # FP4 experts run on bf16 MFMA
-KERNEL_SOURCES = ("mixture_experts_ffn_route_amd/csrc/experts.hip",)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+# sources of the grouped GEMM kernels a workload's GEMM1 runs on (a counter
+# profile is only used while they are unchanged)
+KERNEL_SOURCES = {
+    "bf16": ("mixture_experts_ffn_route_amd/csrc/experts.hip",
+             "mixture_experts_ffn_route_amd/csrc/gemm.h"),
+    "mx": ("mixture_experts_ffn_route_amd/csrc/experts_mx.hip",
+           "mixture_experts_ffn_route_amd/csrc/gemm.h"),
+}
+
+
+def gemm_kind(cfg):
+    return "mx" if cfg.act_quant == "mxfp8" else "bf16"
+
+
+def mfma_peak(cfg):
+    """Dense MFMA peak of the dtype the expert contractions run in: FP8 x FP4
+    scaled MFMA (FP8 rate) on MXFP8 activations, bf16 otherwise (FP4 experts
+    on bf16 activations are decoded to bf16 in registers), fp32 for the fp32
+    layer (plain FMA)."""
+    if cfg.act_quant == "mxfp8":
+        return MFMA_PEAK_TFLOPS["fp8"]
+    return MFMA_PEAK_TFLOPS["f32" if cfg.act_dtype == "f32" else "bf16"]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(kind="bf16"):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -110,7 +131,7 @@ def roofline_entry(flops, nbytes, seconds, peak_tflops):
             "frac": round(ach / peak_tflops, 4)}
 
 
-def load_traffic(workload_name, kernel="gemm1"):
+def load_traffic(workload_name, kind="bf16"):
     """HBM bytes per launch measured with rocprofv3 counters, if they were
     taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", f"grouped_gemm1_{workload_name}_traffic.json")
@@ -119,7 +140,7 @@ def load_traffic(workload_name, kernel="gemm1"):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -306,7 +327,7 @@ def main():
     layer = build_layer(wl, dev, B, synth)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t:.1f} s; timing {args.steps} steps after {args.warmup} warmup")
-    peak = MFMA_PEAK_TFLOPS[wl.cfg.expert_dtype if wl.cfg.expert_dtype == "fp4" else wl.cfg.act_dtype]
+    peak = mfma_peak(wl.cfg)
     rcfg, rlayer = run_weights(wl, layer, B, args.layout)
     torch.cuda.synchronize()
     ms, stage_ms, counts = time_workload(wl, rlayer, args.steps, args.warmup, B, torch, rcfg)
@@ -337,7 +358,7 @@ def main():
     g1 = rep["gemm1"]
     out["roofline"] = {"kernel": "grouped_gemm1 (gate|up + SwiGLU)", "bound": g1["bound"],
                        "achieved": g1["achieved"], "peak": g1["peak"], "unit": g1["unit"],
-                       "frac": g1["frac"], "traffic": load_traffic(wl.name),
+                       "frac": g1["frac"], "traffic": load_traffic(wl.name, gemm_kind(wl.cfg)),
                        "algorithmic_bytes": g1["bytes"], "algorithmic_flops": g1["flops"],
                        "avg_ms": g1["ms"]}
     out["layer_roofline"] = {**rep["layer"], "mfma_frac": rep["layer_mfma_frac"],
@@ -356,11 +377,11 @@ def main():
         else:
             log(f"generating {name} inputs")
             c2cfg, l2 = run_weights(w2, build_layer(w2, dev, B, synth), B, args.layout)
-        p2 = MFMA_PEAK_TFLOPS[w2.cfg.expert_dtype if w2.cfg.expert_dtype == "fp4" else w2.cfg.act_dtype]
+        p2 = mfma_peak(w2.cfg)
         ms2, st2, c2 = time_workload(w2, l2, args.steps, args.warmup, B, torch, c2cfg)
         r2 = workload_report(w2, ms2, st2, c2, p2)
         r2["roofline"] = {k: r2["gemm1"][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
-        r2["roofline"]["traffic"] = load_traffic(name)
+        r2["roofline"]["traffic"] = load_traffic(name, gemm_kind(w2.cfg))
         reports[name] = r2
         log(f"{name}: {r2['ms_per_step']} ms/step, {r2['tokens_per_s']} tokens/s, stages {r2['stage_ms']}")
         del l2

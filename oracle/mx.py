@@ -19,11 +19,11 @@ and saturated to +-448.  An all-zero block gets X = 0.  E4M3 (OCP): bias 7,
 normals 1.m x 2^(e-7) for e = 1..15 except the NaN codes S.1111.111,
 subnormals m/8 x 2^-6.
 
-Pins: tests/test_oracle_mx.py (the full E4M3 value table against its
-definition, hand-worked blocks, round-half-even at midpoints, saturation, the
-bound |decode(q(v)) - v| <= 2^-4 |v| above the subnormal range, the layer
-reducing to the bf16-activation layer when every activation is exactly
-representable).
+Pins: tests/test_oracle_mx.py (the full E4M3 value table and the encoder's
+round-half-even and saturation against torch's float8_e4m3fn cast,
+hand-worked blocks, the bound |decode(q(v)) - v| <= 2^-4 |v| above the
+subnormal range, and the layer against a per-token composition that
+quantises with torch's E4M3 cast).
 """
 
 import math
