@@ -94,7 +94,9 @@ typedef enum {
                                  the stored FP4 codes on the scaled MFMA; needs
                                  expert_dtype FP4_E2M1, act_dtype BF16,
                                  dim % 128 == 0, moe_inter_dim % 128 == 0.  The
-                                 shared expert keeps bf16 activations.         */
+                                 shared expert keeps bf16 activations.  The
+                                 FP8 computation of FP4 experts: "From One
+                                 Giant FFN to 384 Tiny Experts", Ch.11.6.      */
 } moe_act_quant;
 
 /* Layer configuration.  Field names follow the model arguments of the
