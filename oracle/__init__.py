@@ -33,7 +33,8 @@ closed forms, brute force, library routines or hand-derived fixtures.
 from .route import (affinity, selection_keys, learned_gate, hash_gate, ngram_hash_gate,
                     smallest_primes_above)
 from .balance import load_stats, bias_update
-from .mx import mxfp8_quantize, mxfp8_decode, layer_forward_mx, E4M3_VALUES
+from .mx import (mxfp8_quantize, mxfp8_decode, layer_forward_mx, E4M3_VALUES,
+                 fp4_to_fp8_blocks, fp8_blocks_decode)
 from .permute import permute
 from .ffn import swiglu_expert, layer_forward, dense_map_forward, fp4_decode, E2M1_VALUES
 from .tid2eid import (tid2eid_greedy, tid2eid_greedy_order, tid2eid_multistart, tid2eid_objective,
@@ -43,6 +44,7 @@ __all__ = [
     "affinity", "selection_keys", "learned_gate", "hash_gate", "ngram_hash_gate",
     "smallest_primes_above", "load_stats", "bias_update",
     "mxfp8_quantize", "mxfp8_decode", "layer_forward_mx", "E4M3_VALUES",
+    "fp4_to_fp8_blocks", "fp8_blocks_decode",
     "permute",
     "swiglu_expert", "layer_forward", "dense_map_forward", "fp4_decode", "E2M1_VALUES",
     "tid2eid_greedy", "tid2eid_greedy_order", "tid2eid_multistart", "tid2eid_objective",

@@ -19,16 +19,27 @@ and saturated to +-448.  An all-zero block gets X = 0.  E4M3 (OCP): bias 7,
 normals 1.m x 2^(e-7) for e = 1..15 except the NaN codes S.1111.111,
 subnormals m/8 x 2^-6.
 
+The pages' training-time form of "computed in FP8" re-dequantises the FP4
+weights to E4M3 in 128 x 128 blocks and states that the round trip is
+lossless while the sub-block scale ratios stay within a bound
+(fp4_to_fp8_blocks).  With the block scale chosen as the largest nonzero
+sub-block scale over 2^6, every E2M1 value of a sub-block whose scale is at
+most 2^14 below that maximum is an exact E4M3 value; larger spreads round.
+
 Pins: tests/test_oracle_mx.py (the full E4M3 value table and the encoder's
 round-half-even and saturation against torch's float8_e4m3fn cast,
 hand-worked blocks, the bound |decode(q(v)) - v| <= 2^-4 |v| above the
 subnormal range, and the layer against a per-token composition that
-quantises with torch's E4M3 cast).
+quantises with torch's E4M3 cast; the FP4 -> FP8 block re-dequantisation by
+the exact round trip against fp4_decode at spreads up to 2^14, the first
+lossy spread 2^15, and hand-worked codes).
 """
 
 import math
 
 import numpy as np
+
+from .ffn import E2M1_VALUES
 
 E4M3_MAX = 448.0
 
@@ -84,6 +95,55 @@ def mxfp8_decode(codes, scales):
     scales = np.asarray(scales, dtype=np.int64)
     vals = E4M3_VALUES[codes]
     return vals * np.repeat(2.0 ** (scales - 127), 32, axis=1)
+
+
+def fp4_to_fp8_blocks(packed, scales, block=128):
+    """The FP4 -> FP8 re-dequantisation of one [N, K] weight matrix: E2M1 codes
+    (two per byte, low nibble first) with one E8M0 scale per 32 inputs become
+    E4M3 codes with one E8M0 scale per `block` x `block` block.
+
+    Block scale byte B = max(s_max - 6, 0), s_max the largest scale byte among
+    the block's 32-input sub-blocks that hold a nonzero code (127 for a block
+    of zeros): the largest E2M1 magnitude 6 times 2^(s_max - B) = 384 fits
+    E4M3.  Element code = nearest E4M3 value to e2m1 * 2^(s - B).  A block is
+    lossless when every element's code decodes to exactly its FP4 value.
+
+    Returns (codes uint8 [N, K], block_scales uint8 [N/block, K/block],
+    lossless bool [N/block, K/block])."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.int64)
+    N, K = packed.shape[0], packed.shape[1] * 2
+    nib = np.empty((N, K), dtype=np.uint8)
+    nib[:, 0::2] = packed & 0xF
+    nib[:, 1::2] = packed >> 4
+    e2m1 = E2M1_VALUES[nib]
+    nonzero_sub = (nib & 0x7).reshape(N, K // 32, 32).any(axis=2)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    bsc = np.zeros((N // block, K // block), dtype=np.uint8)
+    lossless = np.zeros((N // block, K // block), dtype=bool)
+    sb = block // 32
+    for bi in range(N // block):
+        for bj in range(K // block):
+            r = slice(bi * block, (bi + 1) * block)
+            sub = scales[r, bj * sb:(bj + 1) * sb]
+            nz = nonzero_sub[r, bj * sb:(bj + 1) * sb]
+            s_max = int(sub[nz].max()) if nz.any() else 127
+            B = max(s_max - 6, 0)
+            c = slice(bj * block, (bj + 1) * block)
+            v = e2m1[r, c] * 2.0 ** (np.repeat(sub, 32, axis=1) - B)
+            q = e4m3_encode(v)
+            codes[r, c] = q
+            bsc[bi, bj] = B
+            lossless[bi, bj] = bool(np.all(E4M3_VALUES[q] == v))
+    return codes, bsc, lossless
+
+
+def fp8_blocks_decode(codes, block_scales, block=128):
+    """Values of E4M3 codes [N, K] with one E8M0 scale per block x block block."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    bs = np.asarray(block_scales, dtype=np.int64)
+    scale = np.repeat(np.repeat(2.0 ** (bs - 127), block, axis=0), block, axis=1)
+    return E4M3_VALUES[codes] * scale
 
 
 def _swiglu(h_g, h_u, limit):

@@ -88,3 +88,91 @@ def test_layer_forward_mx_against_an_independent_composition():
             h = g / (1 + np.exp(-g)) * u
             ref[t] += w[t, j] * (_torch_mx(h[None])[0] @ wd.T)
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---- FP4 -> FP8 re-dequantisation in 128 x 128 blocks ----
+
+def _fp4_matrix(rng, N, K, scales):
+    packed = rng.integers(0, 256, size=(N, K // 2)).astype(np.uint8)
+    return packed, np.asarray(scales, dtype=np.uint8)
+
+
+def test_fp8_blocks_round_trip_is_exact_within_the_bound():
+    """Every sub-block scale within 2^14 of its block's largest: the E4M3
+    codes times the block scale give back the FP4 values exactly."""
+    rng = np.random.default_rng(3)
+    N, K = 256, 384
+    top = rng.integers(100, 150, size=(N // 128, K // 128))
+    spread = rng.integers(0, 15, size=(N, K // 32))
+    scales = np.repeat(np.repeat(top, 128, axis=0), 4, axis=1) - spread
+    packed, scales = _fp4_matrix(rng, N, K, scales)
+    codes, bsc, lossless = oracle.fp4_to_fp8_blocks(packed, scales)
+    assert lossless.all()
+    np.testing.assert_array_equal(oracle.fp8_blocks_decode(codes, bsc),
+                                  oracle.fp4_decode(packed, scales))
+    # decode against torch's E4M3 values, independently of the oracle's table
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    scale = np.repeat(np.repeat(2.0 ** (bsc.astype(np.int64) - 127), 128, 0), 128, 1)
+    np.testing.assert_array_equal(t * scale, oracle.fp4_decode(packed, scales))
+
+
+def test_fp8_blocks_first_lossy_spread():
+    """A spread of 2^15 pushes 0.5 and 1.5 of the small sub-block below E4M3's
+    2^-9 step: those round (half to even) and the block is flagged."""
+    N, K = 128, 128
+    scales = np.full((N, K // 32), 140, dtype=np.uint8)
+    packed = np.zeros((N, K // 2), dtype=np.uint8)
+    packed[0, 0] = 0x06                      # element (0, 0) = 4 in sub-block (0, 0), scale 140
+    scales[1, 0] = 140 - 15
+    packed[1, 0] = 0x31                      # (1, 0) = 0.5, (1, 1) = 1.5 at scale 125
+    codes, bsc, lossless = oracle.fp4_to_fp8_blocks(packed, scales)
+    assert bsc[0, 0] == 134 and not lossless[0, 0]
+    # 0.5 * 2^-9 = 2^-10: halfway between 0 and 2^-9 -> code 0 (even)
+    # 1.5 * 2^-9 = 3 * 2^-10: halfway between 1 and 2 (x 2^-9) -> code 2 (even)
+    assert codes[1, 0] == 0x00 and codes[1, 1] == 0x02
+    scales[1, 0] = 140 - 14
+    codes, bsc, lossless = oracle.fp4_to_fp8_blocks(packed, scales)
+    assert lossless[0, 0] and codes[1, 0] == 0x01 and codes[1, 1] == 0x03
+
+
+def test_fp8_blocks_hand_worked():
+    N, K = 128, 256
+    scales = np.full((N, K // 32), 127, dtype=np.uint8)
+    packed = np.zeros((N, K // 2), dtype=np.uint8)
+    packed[5, 0] = 0xD7                      # (5,0) = 6, (5,1) = -3, sub-block scale 127
+    scales[9, 2] = 120
+    packed[9, 32] = 0x01                     # (9,64) = 0.5, sub-block scale 120
+    scales[20, 1] = 250                      # a sub-block of zeros does not set the block scale
+    codes, bsc, lossless = oracle.fp4_to_fp8_blocks(packed, scales)
+    # block scale 127 - 6 = 121: 6 * 2^6 = 384 = 1.5 * 2^8 -> 0x7C; -3 * 2^6 = -192 -> 0xF4;
+    # 0.5 * 2^-1 = 2^-2 -> 0x28.  The all-zero second block column takes s_max = 127 too
+    # (its scale-250 sub-block holds only zeros).
+    assert bsc[0, 0] == 121 and bsc[0, 1] == 121 and lossless.all()
+    assert (codes[5, 0], codes[5, 1], codes[9, 64]) == (0x7C, 0xF4, 0x28)
+    assert np.count_nonzero(codes) == 3
+
+
+def test_fp8_weight_layer_equals_fp4_layer_when_lossless():
+    rng = np.random.default_rng(4)
+    T, d, I, E, k = 7, 128, 128, 3, 2
+    mats = []
+    for _ in range(E):
+        trio = []
+        for (n, kk) in ((I, d), (I, d), (d, I)):
+            sc = 120 + rng.integers(0, 6, size=(n, kk // 32))
+            p, s = _fp4_matrix(rng, n, kk, sc)
+            trio.append((p, s))
+        mats.append(trio)
+    fp4 = lambda e: tuple(oracle.fp4_decode(p, s) for p, s in mats[e])
+    def fp8(e):
+        out = []
+        for p, s in mats[e]:
+            c, b, ok = oracle.fp4_to_fp8_blocks(p, s)
+            assert ok.all()
+            out.append(oracle.fp8_blocks_decode(c, b))
+        return tuple(out)
+    x = rng.normal(size=(T, d))
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    w = rng.uniform(0.1, 1, size=(T, k))
+    np.testing.assert_array_equal(oracle.layer_forward_mx(x, w, idx, fp8, None, 10.0),
+                                  oracle.layer_forward_mx(x, w, idx, fp4, None, 10.0))
