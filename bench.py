@@ -69,7 +69,9 @@ def algorithmic_counts(wl, counts):
     cfg, T = wl.cfg, wl.T
     d, I, E, k = cfg.dim, cfg.moe_inter_dim, cfg.n_routed_experts, cfg.n_activated_experts
     eb = 4 if cfg.act_dtype == "f32" else 2
-    if cfg.expert_dtype == "fp4":
+    if wl.fp8_weights:
+        mat = I * d * (1.0 + 1.0 / 16384.0)       # E4M3 codes + one scale byte per 128x128
+    elif cfg.expert_dtype == "fp4":
         mat = I * d * (0.5 + 1.0 / 32.0)          # codes + one scale byte per 32
     else:
         mat = I * d * eb
@@ -158,7 +160,13 @@ def build_layer(wl, dev, B, synth):
 def run_weights(wl, layer, B, layout):
     """(config, layer) the timed steps use: the expert matrices rewritten once
     into the tiled layout (a load-time storage format) unless `layout` is
-    "rows" or the layer is fp32."""
+    "rows" or the layer is fp32; FP4 experts re-dequantised once to FP8 for
+    the FP8-weight workloads (a load-time format too)."""
+    if wl.fp8_weights:
+        cfg8, layer8, lossy = B.redequant_layer(wl.cfg, layer)
+        if lossy:
+            log(f"{wl.name}: {lossy} lossy 128x128 blocks in the FP8 re-dequantisation")
+        return cfg8, layer8
     if layout == "rows" or wl.cfg.act_dtype != "bf16":
         return wl.cfg, layer
     return B.pack_layer(wl.cfg, layer)
@@ -283,7 +291,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill")
     ap.add_argument("--decode", default="v3_decode", help="second workload ('' to skip)")
-    ap.add_argument("--extra", default="hash_bf16,ngram_bf16,v41_flash_fp4,v41_flash_fp4_mx,tiny_fp32",
+    ap.add_argument("--extra", default="hash_bf16,ngram_bf16,v41_flash_fp4,v41_flash_fp4_mx,"
+                                      "v41_flash_fp8,tiny_fp32",
                     help="comma-separated further workloads to report ('' for none)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=96,
                     help="tokens of the batch the CPU oracle is timed on (about 10 s)")

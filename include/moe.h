@@ -75,7 +75,12 @@ typedef enum {
 typedef enum {
   MOE_DTYPE_F32 = 0,
   MOE_DTYPE_BF16 = 1,
-  MOE_DTYPE_FP4_E2M1 = 2      /* routed experts only; see conventions above    */
+  MOE_DTYPE_FP4_E2M1 = 2,     /* routed experts only; see conventions above    */
+  MOE_DTYPE_FP8_E4M3_B128 = 3 /* routed experts only: E4M3 codes in the layout
+                                 moe_redequant_fp8 writes, one E8M0 scale per
+                                 128 x 128 block (moe_weights.s_gate/s_up/s_down
+                                 point to the [E, out/128, in/128] scales);
+                                 needs act_quant MXFP8 and weight_layout TILED */
 } moe_dtype;
 
 typedef enum {
@@ -226,6 +231,33 @@ int moe_build_tid2eid(const double *p, int64_t m, int32_t n, int32_t k,
  * src member is set, or an fp32 layer; validation as moe_validate_config. */
 int moe_pack_weights(const moe_config *cfg, const moe_weights *src,
                      const moe_weights *dst, void *stream);
+
+/* FP4 -> FP8 re-dequantisation of expert weights ("From One Giant FFN to 384
+ * Tiny Experts", Ch.11.6: FP4 weights in 1x32 sub-blocks dequantised to FP8
+ * E4M3 in 128 x 128 blocks for computation, lossless while the sub-block
+ * scale ratios stay within a bound).
+ *   codes         n_mat consecutive FP4 matrices [N, K/2] bytes, row layout
+ *                 (conventions above)
+ *   scales        their E8M0 scales [N, K/32]
+ *   fp8           out: E4M3 codes, n_mat x N x K bytes in the FP8 expert
+ *                 layout: per matrix, 16-row block nb and 128-input stage st,
+ *                 a 2 KB block at byte ((nb*(K/128) + st)*2048 whose byte
+ *                 ((h*4 + q)*16 + c)*16 + i is the element of row 16nb + c,
+ *                 input 128st + 64h + 16q + i
+ *   block_scales  out: E8M0 [n_mat, N/128, K/128]: B = s_max - 6 floored at
+ *                 0, s_max the largest scale among the block's 32-input
+ *                 sub-blocks holding a nonzero code (127 if none)
+ *   lossy         out: uint8 [n_mat, N/128, K/128], 1 where some element's
+ *                 E4M3 code (the nearest value to e2m1 x 2^(s - B), ties to
+ *                 even, saturating at 448) is not exactly its FP4 value --
+ *                 exactly the blocks with a nonzero sub-block whose scale is
+ *                 more than 2^14 below s_max -- else 0
+ * Device pointers, enqueued on `stream` (hipStream_t or NULL).  N and K must
+ * be positive multiples of 128 (MOE_ERR_UNSUPPORTED otherwise); NULL
+ * pointers or n_mat < 0 give MOE_ERR_INVALID_ARG. */
+int moe_redequant_fp8(const uint8_t *codes, const uint8_t *scales, int64_t n_mat, int32_t N,
+                      int32_t K, uint8_t *fp8, uint8_t *block_scales, uint8_t *lossy,
+                      void *stream);
 
 /* Multi-start variant of moe_build_tid2eid (same page, "Reference
  * implementation": tokens taken in a random order instead of by decreasing

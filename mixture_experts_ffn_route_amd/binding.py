@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout",
     "moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_profiled",
     "moe_pack_weights", "moe_build_tid2eid_multistart", "moe_update_bias", "moe_probe_read",
-    "moe_probe_mfma",
+    "moe_probe_mfma", "moe_redequant_fp8",
 )
 MOE_STAGES = ("route", "permute", "gemm1", "gemm2", "combine")
 
@@ -84,6 +84,7 @@ def _load():
     lib.moe_update_bias.argtypes = [cfgp, vp, i64, ctypes.c_float, vp, vp, vp]
     lib.moe_probe_read.argtypes = [vp, i64, vp, vp]
     lib.moe_probe_mfma.argtypes = [i32, i32, vp, vp, vp]
+    lib.moe_redequant_fp8.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp]
     lib.moe_forward_profiled.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t,
                                          ctypes.POINTER(ctypes.c_void_p), vp]
     for f in ("moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout", "moe_route",
@@ -241,6 +242,41 @@ def pack_layer(cfg: MoEConfig, layer: dict, stream=None):
             out[n] = torch.empty_like(layer[n])
     moe_pack_weights(cfg, layer, out, stream)
     return replace(cfg, weight_layout="tiled"), out
+
+
+def moe_redequant_fp8(codes, scales, n_mat: int, N: int, K: int, fp8, block_scales, lossy,
+                      stream=None):
+    """FP4 [n_mat, N, K/2] codes + [n_mat, N, K/32] scales -> E4M3 codes in the
+    FP8 expert layout, [n_mat, N/128, K/128] block scales and lossy flags."""
+    _check(_lib.moe_redequant_fp8(_ptr(codes), _ptr(scales), n_mat, N, K, _ptr(fp8),
+                                  _ptr(block_scales), _ptr(lossy), _stream(stream)),
+           "moe_redequant_fp8")
+
+
+def redequant_layer(cfg: MoEConfig, layer: dict, stream=None):
+    """(cfg with FP8 experts and tiled weights, a copy of the FP4 `layer` whose
+    routed matrices are re-dequantised to FP8 by moe_redequant_fp8 and whose
+    shared matrices are tiled by moe_pack_weights, total lossy block count)."""
+    if cfg.expert_dtype != "fp4" or cfg.weight_layout != "rows":
+        raise ValueError("redequant_layer takes an FP4 layer in the row layout")
+    out = dict(layer)
+    shared = {n: layer.get(n) for n in ("sh_gate", "sh_up", "sh_down")}
+    if cfg.n_shared_experts:
+        dst = {n: torch.empty_like(v) for n, v in shared.items()}
+        moe_pack_weights(cfg, shared, dst, stream)
+        out.update(dst)
+    E, d, I = cfg.n_routed_experts, cfg.dim, cfg.moe_inter_dim
+    dev = layer["w_gate"].device
+    lossy_total = 0
+    for n, sn, N, K in (("w_gate", "s_gate", I, d), ("w_up", "s_up", I, d),
+                        ("w_down", "s_down", d, I)):
+        codes = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+        bsc = torch.empty((E, N // 128, K // 128), dtype=torch.uint8, device=dev)
+        lossy = torch.empty_like(bsc)
+        moe_redequant_fp8(layer[n], layer[sn], E, N, K, codes, bsc, lossy, stream)
+        out[n], out[sn] = codes, bsc
+        lossy_total += int(lossy.sum())
+    return replace(cfg, expert_dtype="fp8", weight_layout="tiled"), out, lossy_total
 
 
 def moe_forward(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, ws, stream=None,

@@ -9,7 +9,7 @@ from dataclasses import dataclass, field, replace
 
 SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
 ROUTE = {"learned": 0, "hash": 1, "ngram": 2}
-DTYPE = {"f32": 0, "bf16": 1, "fp4": 2}
+DTYPE = {"f32": 0, "bf16": 1, "fp4": 2, "fp8": 3}   # fp8: E4M3 in 128x128 blocks (re-dequantised FP4)
 LAYOUT = {"rows": 0, "tiled": 1}
 ACT_QUANT = {"none": 0, "mxfp8": 1}
 
@@ -54,6 +54,7 @@ class Workload:
     seed: int = 0
     x_rows: int = 0              # draw x with this many rows, keep the first T
     seq_len: int = 0             # 2-gram hash: tokens per sequence (0: one sequence)
+    fp8_weights: bool = False    # FP4 layer run on its FP8 re-dequantisation (moe_redequant_fp8)
     description: str = ""
 
 
@@ -101,8 +102,13 @@ V41_FLASH_FP4_MX = replace(
     description="V4.1-Flash shape with the routed FP4 experts on MXFP8 activations "
                 "(E4M3 + E8M0/32) and the scaled MFMA")
 
+V41_FLASH_FP8 = replace(
+    V41_FLASH_FP4_MX, name="v41_flash_fp8", fp8_weights=True,
+    description="V4.1-Flash shape with the FP4 routed experts re-dequantised to FP8 E4M3 in "
+                "128x128 blocks, on MXFP8 activations (FP8 x FP8 scaled MFMA)")
+
 FULL_WORKLOADS = {w.name: w for w in (TINY_FP32, HASH_BF16, V3_PREFILL, V3_DECODE, V41_FLASH_FP4,
-                                      NGRAM_BF16, V41_FLASH_FP4_MX)}
+                                      NGRAM_BF16, V41_FLASH_FP4_MX, V41_FLASH_FP8)}
 
 # Reduced versions: the same structure at sizes the oracle finishes in
 # seconds while still spanning several GEMM tiles, slabs and a ragged tail.
@@ -148,6 +154,23 @@ SMALL_WORKLOADS = {
         replace(V41_FLASH_FP4.cfg, dim=384, moe_inter_dim=256, n_routed_experts=24,
                 act_quant="mxfp8"),
         T=300, x_scale=20.0, description="MXFP8 activations with the clamp firing; 3 k-stages"),
+    "fp8_mx_small": Workload(
+        "fp8_mx_small",
+        replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48,
+                act_quant="mxfp8"),
+        T=157, fp8_weights=True,
+        description="FP4 experts re-dequantised to FP8 (128x128 blocks) on MXFP8 activations"),
+    "fp8_mx_decode": Workload(
+        "fp8_mx_decode",
+        replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=256, n_routed_experts=48,
+                act_quant="mxfp8"),
+        T=9, fp8_weights=True, description="FP8 weights, decode batch (run as 4-block tiles)"),
+    "fp8_mx_clamp": Workload(
+        "fp8_mx_clamp",
+        replace(V41_FLASH_FP4.cfg, dim=384, moe_inter_dim=256, n_routed_experts=24,
+                act_quant="mxfp8"),
+        T=300, x_scale=20.0, fp8_weights=True,
+        description="FP8 weights, clamp firing, 3 k-stages, two column slabs"),
     "fp4_clamp_small": Workload(
         "fp4_clamp_small",
         replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=128, n_routed_experts=48),

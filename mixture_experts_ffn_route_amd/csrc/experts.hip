@@ -600,8 +600,12 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   }
 
   const int mb = p.tile_rows / 16;
-  const bool fp4 = p.expert_dtype == MOE_DTYPE_FP4_E2M1;
+  // low-precision routed experts (FP4, or FP8 re-dequantised from FP4): the
+  // shared expert runs as its own bf16 launch
+  const bool fp4 = p.expert_dtype == MOE_DTYPE_FP4_E2M1 ||
+                   p.expert_dtype == MOE_DTYPE_FP8_E4M3_B128;
   GemmArgs a = {};
+  a.b_fp8 = p.expert_dtype == MOE_DTYPE_FP8_E4M3_B128 ? 1 : 0;
   a.E = p.E;
   a.tiles = p.tiles;
   a.tile_count = p.tile_count;

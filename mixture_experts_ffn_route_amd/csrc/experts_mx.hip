@@ -19,30 +19,11 @@
 // words copied global -> LDS, FP4 codes and scales into a register ring,
 // static waits, refills spread over the MFMA chunks.
 
+#include "fp8.h"
 #include "gemm.h"
 
 namespace moe {
 namespace {
-
-// Nearest E4M3 (OCP) code to v, ties to even mantissa, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (!(a < 448.f)) {
-    code = 0x7Eu;                              // 1.75 x 2^8
-  } else if (a < 0.015625f) {                  // below 2^-6: multiples of 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.f);   // 8 -> 0x08 = 2^-6
-  } else {
-    const uint32_t f = __float_as_uint(a);
-    uint32_t q = f >> 20;                      // fp32 exponent and top 3 mantissa bits
-    const uint32_t rem = f & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-    code = q - (120u << 3);                    // rebias 127 -> 7
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return sign | code;
-}
 
 // One thread per 32-input block (rows are contiguous, so block i of the
 // flattened array is row i / (K/32)): shared exponent floor(log2(amax)) - 8
@@ -313,7 +294,11 @@ constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 struct MxRing {
   uint8_t *a[4];
   uint8_t *b[8];
+  uint8_t *bs;    // FP8 weights: the slab's block scales, [matrix][stage]
 };
+
+// Most 128-input stages the FP8-weight form keeps block scales for (K <= 32768).
+constexpr int kMxF8MaxStages = 256;
 
 // Row-split tile for tiles of 4 and more row blocks.  Each wave owns MW =
 // MBE/WAVES row blocks and every column of the slab: SC 16-column blocks of
@@ -329,21 +314,28 @@ struct MxRing {
 // and its weight copies last: the in-order count then lets the wait for a
 // stage's activations leave the far weight copies in flight.
 //
-// LDS form of a weight fragment.  Tiled weights: the 16-byte chunk (t, g, p)
+// FP8 weights (F8, re-dequantised from FP4 by moe_redequant_fp8): a fragment
+// is 2 KB stored in operand order -- lane (c, q) reads 16 bytes at
+// (q*16 + c)*16 and 16 at 1024 + (q*16 + c)*16 -- and is copied as two 1 KB
+// units; its scale is the one E8M0 byte of the 128 x 128 block, the same for
+// the whole slab and stage, kept in LDS for all stages of the tile.
+//
+// LDS form of an FP4 weight fragment.  Tiled weights: the 16-byte chunk (t, g, p)
 // of the stage (64-input tile t, 8-byte group g, column pair p) is stored at
 // chunk t*32 + (g%2)*16 + (g/2)*8 + p, so the two 8-byte pieces a lane needs
 // sit 256 bytes apart and 32 lanes of a read touch all 64 banks once.  Row
 // weights: chunk (column r, 32-input part c) at chunk 16c + r, the lane's 16
 // bytes contiguous.  Weight scales: the 64 bytes of the stage in the global
 // order (tiled: [tile][column][block%2], rows: [column][block]).
-template <int WAVES, int NB, int SC, int MBE, int NSA, int NSB, int A_MAX>
+template <int WAVES, int NB, int SC, int MBE, int NSA, int NSB, int A_MAX, bool F8>
 __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx &t,
                                                 const MxRing &ring) {
   constexpr int BK = 128;
   constexpr int MW = MBE / WAVES;                  // row blocks of one wave
   constexpr int NFR = NB * SC;                     // weight fragments per stage
-  constexpr int NBU = (NFR + WAVES - 1) / WAVES;   // fragment copies per wave
-  constexpr int NSG = (NFR + 3) / 4;               // weight-scale copies (4 fragments each)
+  constexpr int FRAG = F8 ? 2048 : 1024;           // bytes per fragment in LDS
+  constexpr int NBU = (NFR * (FRAG / 1024) + WAVES - 1) / WAVES;   // 1 KB copies per wave
+  constexpr int NSG = F8 ? 0 : (NFR + 3) / 4;      // weight-scale copies (4 fragments each)
   constexpr int NSU = (NSG + WAVES - 1) / WAVES;   // per wave
   constexpr int AS_OFF = A_MAX * 2 * 1024;         // activation slot: units, then scales
   constexpr int S_OFF = NBU * WAVES * 1024;        // weight slot: fragments, then scales
@@ -400,15 +392,22 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
     assrc = g.Asc + src * KS;
   }
   // weight copies: unit u = wave + WAVES*i is fragment (u / SC, u % SC)
-  const int64_t bst = tiled ? 1024 : 64;
+  // (FP8: half u % 2 of fragment u / 2)
+  const int64_t bst = F8 ? 2048 : (tiled ? 1024 : 64);
   const int64_t sst = tiled ? 64 : 4;
   const uint8_t *bsrc[NBU];
 #pragma unroll
   for (int i = 0; i < NBU; ++i) {
     const int u0 = wave + WAVES * i;
-    const int u = u0 < NFR ? u0 : 0;
-    const int b = u / SC, cb = u - b * SC;
+    const int u = u0 < NFR * (FRAG / 1024) ? u0 : 0;
+    const int f = F8 ? u >> 1 : u;
+    const int b = f / SC, cb = f - b * SC;
     const int64_t nb = (col0 >> 4) + cb;
+    if (F8) {
+      const uint8_t *mat = (const uint8_t *)g.B[b] + (int64_t)t.grp * N * K;
+      bsrc[i] = mat + nb * (K / 128) * 2048 + (u & 1) * 1024 + lane * 16;
+      continue;
+    }
     const uint8_t *mat = (const uint8_t *)g.B[b] + (int64_t)t.grp * N * (K / 2);
     if (tiled) {
       const int tt = lane >> 5, gg = ((lane >> 3) & 1) * 2 + ((lane >> 4) & 1), pp = lane & 7;
@@ -417,7 +416,7 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
       bsrc[i] = mat + (nb * 16 + (lane & 15)) * (K / 2) + 16 * (lane >> 4);
     }
   }
-  const uint8_t *ssrc[NSU];
+  const uint8_t *ssrc[NSU > 0 ? NSU : 1];
 #pragma unroll
   for (int i = 0; i < NSU; ++i) {
     const int j0 = wave + WAVES * i;
@@ -436,9 +435,10 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
   const int a_lo = (r16 >> 3) * 1024 + (rr * 8 + (q ^ rr)) * 16;
   const int a_hi = (r16 >> 3) * 1024 + (rr * 8 + ((4 + q) ^ rr)) * 16;
   const int a_sc = AS_OFF + wave * 256 + r16 * 4 + q;
-  const int boff0 = tiled ? ((q >> 1) * 32 + (q & 1) * 8 + (r16 >> 1)) * 16 + (r16 & 1) * 8
-                          : (q * 16 + r16) * 16;
-  const int boff1 = boff0 + (tiled ? 256 : 8);
+  const int boff0 = F8 ? (q * 16 + r16) * 16
+                 : tiled ? ((q >> 1) * 32 + (q & 1) * 8 + (r16 >> 1)) * 16 + (r16 & 1) * 8
+                         : (q * 16 + r16) * 16;
+  const int boff1 = boff0 + (F8 ? 1024 : tiled ? 256 : 8);
   const int soff = S_OFF + (tiled ? (q >> 1) * 32 + r16 * 2 + (q & 1) : r16 * 4 + q);
 
   f32x4 acc[MW][NB][SC];
@@ -451,6 +451,15 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
 
   const int nst = K / BK;
   const int last = nst - 1;
+  if constexpr (F8) {
+    // block scales of this slab (one 128-row block of each matrix) for every stage
+    const int br = col0 >> 7;
+    for (int i = threadIdx.x; i < NB * nst; i += WAVES * 64) {
+      const int b = i / nst, st = i - b * nst;
+      ring.bs[i] = g.S[b][((int64_t)t.grp * (N / 128) + br) * nst + st];
+    }
+    __syncthreads();
+  }
   // copy qq of a stage: activations of stage STA into slot SA (qq < VMA),
   // then weights of stage STB into slot SB
   auto issue_op = [&](int SA, int STA, int SB, int STB, int qq) {
@@ -485,7 +494,7 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
   // stage with activations in slot pa and weights in slot pb; refills
   // activations of stage nxa into slot (pa+NSA-1)%NSA and weights of stage nxb
   // into slot (pb+NSB-1)%NSB, interleaved with the MFMAs
-  auto compute_stage = [&](int pa, int pb, int nxa, int nxb) {
+  auto compute_stage = [&](int st, int pa, int pb, int nxa, int nxb) {
     const int na = (pa + NSA - 1) % NSA, nb = (pb + NSB - 1) % NSB;
     const uint8_t *aslot = ring.a[pa];
     const uint8_t *bslot = ring.b[pb];
@@ -503,11 +512,24 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
     // weight fragments are read one ahead of their MFMAs
     i32x8 bv[2];
     int sbv[2];
+    int sblk[NB];
+    if constexpr (F8) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sblk[b] = ring.bs[b * nst + st];
+    }
     auto read_frag = [&](int f, int buf) {
-      const uint2 lo = *(const uint2 *)(bslot + f * 1024 + boff0);
-      const uint2 hi = *(const uint2 *)(bslot + f * 1024 + boff1);
-      bv[buf] = i32x8{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y, 0, 0, 0, 0};
-      sbv[buf] = bslot[soff + f * 64];
+      if constexpr (F8) {
+        const u32x4 lo = *(const u32x4 *)(bslot + f * FRAG + boff0);
+        const u32x4 hi = *(const u32x4 *)(bslot + f * FRAG + boff1);
+        bv[buf] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        sbv[buf] = sblk[f / SC];
+      } else {
+        const uint2 lo = *(const uint2 *)(bslot + f * FRAG + boff0);
+        const uint2 hi = *(const uint2 *)(bslot + f * FRAG + boff1);
+        bv[buf] = i32x8{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y, 0, 0, 0, 0};
+        sbv[buf] = bslot[soff + f * 64];
+      }
     };
     read_frag(0, 0);
 #pragma unroll
@@ -517,7 +539,7 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
 #pragma unroll
       for (int m = 0; m < MW; ++m)
         acc[m][b][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            av[m], bv[f & 1], acc[m][b][cb], 0, 4, 0, sa[m], 0, sbv[f & 1]);
+            av[m], bv[f & 1], acc[m][b][cb], 0, F8 ? 0 : 4, 0, sa[m], 0, sbv[f & 1]);
 #pragma unroll
       for (int j = 0; j < ISSUE_PER_FRAG; ++j) {
         const int qq = f * ISSUE_PER_FRAG + j;
@@ -536,7 +558,7 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
       const int st = s0 + p;
       __builtin_amdgcn_s_waitcnt(MOE_VMCNT(WAIT));
       __builtin_amdgcn_s_barrier();
-      compute_stage(p % NSA, p % NSB, st + NSA - 1 < last ? st + NSA - 1 : last,
+      compute_stage(st, p % NSA, p % NSB, st + NSA - 1 < last ? st + NSA - 1 : last,
                     st + NSB - 1 < last ? st + NSB - 1 : last);
     }
   }
@@ -548,7 +570,7 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
     if (st < nst) {
       __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
       __builtin_amdgcn_s_barrier();
-      compute_stage(p % NSA, p % NSB, st + NSA - 1 < last ? st + NSA - 1 : last,
+      compute_stage(st, p % NSA, p % NSB, st + NSA - 1 < last ? st + NSA - 1 : last,
                     st + NSB - 1 < last ? st + NSB - 1 : last);
     }
   }
@@ -592,21 +614,21 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
 template <int WAVES, int MB>
 constexpr int gemm_mx_rs_aslot_bytes() { return MB * 2 * 1024 + WAVES * 256; }
 
-template <int WAVES, int NB, int SC>
+template <int WAVES, int NB, int SC, bool F8>
 constexpr int gemm_mx_rs_bslot_bytes() {
   constexpr int NFR = NB * SC;
-  constexpr int NBU = (NFR + WAVES - 1) / WAVES;
-  constexpr int NSU = ((NFR + 3) / 4 + WAVES - 1) / WAVES;
+  constexpr int NBU = (NFR * (F8 ? 2 : 1) + WAVES - 1) / WAVES;
+  constexpr int NSU = F8 ? 0 : ((NFR + 3) / 4 + WAVES - 1) / WAVES;
   return NBU * WAVES * 1024 + NSU * WAVES * 256;
 }
 
 // Row-split kernel: the tile height is taken as the smallest multiple of
 // WAVES row blocks (and of 4) that holds the tile's rows, up to MB.
-template <int WAVES, int NB, int SC, int MB, int NSA, int NSB, int WPE>
+template <int WAVES, int NB, int SC, int MB, int NSA, int NSB, int WPE, bool F8>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void grouped_gemm_mx_rs(const GemmArgs g) {
   constexpr int SA = gemm_mx_rs_aslot_bytes<WAVES, MB>();
-  constexpr int SB = gemm_mx_rs_bslot_bytes<WAVES, NB, SC>();
+  constexpr int SB = gemm_mx_rs_bslot_bytes<WAVES, NB, SC, F8>();
   constexpr int STEP = WAVES > 4 ? WAVES : 4;
   static_assert(MB % STEP == 0, "tile height in whole steps");
   __shared__ __attribute__((aligned(1024))) uint8_t A0[SA];
@@ -621,29 +643,30 @@ void grouped_gemm_mx_rs(const GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t B5[NSB > 5 ? SB : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t B6[NSB > 6 ? SB : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t B7[NSB > 7 ? SB : 1];
-  const MxRing ring{{A0, A1, A2, A3}, {B0, B1, B2, B3, B4, B5, B6, B7}};
+  __shared__ uint8_t BS[F8 ? NB * kMxF8MaxStages : 1];
+  const MxRing ring{{A0, A1, A2, A3}, {B0, B1, B2, B3, B4, B5, B6, B7}, BS};
   int tile, slab;
   if (!gemm_work_item(g, &tile, &slab)) return;
   TileCtx t = gemm_tile_ctx(g, tile, slab, 1, SC * 16);
   t.col0 = slab * (SC * 16);                // every wave covers the whole slab
   const int nmb = (t.rows + 15) >> 4;
   if (MB <= STEP || nmb <= STEP)
-    gemm_tile_mx_rs<WAVES, NB, SC, STEP, NSA, NSB, MB>(g, t, ring);
+    gemm_tile_mx_rs<WAVES, NB, SC, STEP, NSA, NSB, MB, F8>(g, t, ring);
   else if (MB <= 2 * STEP || nmb <= 2 * STEP)
-    gemm_tile_mx_rs<WAVES, NB, SC, (MB < 2 * STEP ? MB : 2 * STEP), NSA, NSB, MB>(g, t, ring);
+    gemm_tile_mx_rs<WAVES, NB, SC, (MB < 2 * STEP ? MB : 2 * STEP), NSA, NSB, MB, F8>(g, t, ring);
   else if (MB <= 3 * STEP || nmb <= 3 * STEP)
-    gemm_tile_mx_rs<WAVES, NB, SC, (MB < 3 * STEP ? MB : 3 * STEP), NSA, NSB, MB>(g, t, ring);
+    gemm_tile_mx_rs<WAVES, NB, SC, (MB < 3 * STEP ? MB : 3 * STEP), NSA, NSB, MB, F8>(g, t, ring);
   else
-    gemm_tile_mx_rs<WAVES, NB, SC, MB, NSA, NSB, MB>(g, t, ring);
+    gemm_tile_mx_rs<WAVES, NB, SC, MB, NSA, NSB, MB, F8>(g, t, ring);
 }
 
-template <int WAVES, int NB, int SC, int MB, int NSA, int NSB, int WPE>
+template <int WAVES, int NB, int SC, int MB, int NSA, int NSB, int WPE, bool F8 = false>
 hipError_t run_gemm_mx_rs(GemmArgs a, int max_tiles, hipStream_t s) {
   if (a.N % (SC * 16)) return hipErrorInvalidValue;
   a.n_slabs = a.N / (SC * 16);
   const int64_t blocks = gemm_grid_blocks(a, max_tiles);
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_mx_rs<WAVES, NB, SC, MB, NSA, NSB, WPE>),
+  hipLaunchKernelGGL((grouped_gemm_mx_rs<WAVES, NB, SC, MB, NSA, NSB, WPE, F8>),
                      dim3((unsigned)blocks), dim3(WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -698,6 +721,13 @@ hipError_t run_gemm_mx(GemmArgs a, int max_tiles, hipStream_t s) {
 // of up, or 256 down columns (half that when the width does not divide).
 template <int NB, int MB>
 hipError_t run_gemm_mx_mb(GemmArgs a, int max_tiles, hipStream_t s) {
+  if (a.b_fp8) {
+    // FP8 weights (2 KB fragments): 64 gate|up or 128 down columns per slab;
+    // decode tiles run as 4-block tiles
+    constexpr int SC8 = NB == 2 ? 4 : 8;
+    if (a.N % (SC8 * 16) != 0 || a.K / 128 > kMxF8MaxStages) return hipErrorInvalidValue;
+    return run_gemm_mx_rs<4, NB, SC8, (MB < 4 ? 4 : MB), 3, 3, 1, true>(a, max_tiles, s);
+  }
   if constexpr (MB >= 4) {
     constexpr int NARROW = NB == 2 ? 4 : 8;
     constexpr int WIDE = MB <= 12 ? 2 * NARROW : NARROW;

@@ -30,6 +30,8 @@ struct GemmArgs {
   int64_t dense_rows;        // tiles == null: one group of this many rows, cut
   int dense_tile_rows;       //   into tiles of dense_tile_rows rows
   int64_t routed_rows;       // T * k: rows at or above this belong to the shared expert
+  int b_fp8;                 // MX form: B is E4M3 in the FP8 expert layout and S its
+                             //   128 x 128 block scales [E, N/128, K/128]
 };
 
 #define MOE_LDS __attribute__((address_space(3)))

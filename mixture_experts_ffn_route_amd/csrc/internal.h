@@ -88,6 +88,11 @@ int choose_tile_rows(const moe_config &cfg, int64_t T);
 
 hipError_t launch_experts(const ExpertPlan &p, hipStream_t s);
 
+// FP4 -> FP8 E4M3 in 128 x 128 blocks (moe_redequant_fp8).
+hipError_t launch_redequant_fp8(const uint8_t *codes, const uint8_t *scales, int64_t n_mat, int N,
+                                int K, uint8_t *out, uint8_t *bscale, uint8_t *lossy,
+                                hipStream_t s);
+
 // Rewrite `count` consecutive [N, K] expert matrices (bf16 or FP4 codes) or
 // their E8M0 scales (scales = true) from the row layout into the tiled one.
 hipError_t launch_pack_matrix(const void *src, void *dst, int64_t count, int64_t N, int64_t K,

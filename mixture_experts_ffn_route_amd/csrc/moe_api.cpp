@@ -42,7 +42,8 @@ int validate(const moe_config *c) {
   if (c->act_dtype == MOE_DTYPE_F32) {
     if (c->expert_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
   } else if (c->act_dtype == MOE_DTYPE_BF16) {
-    if (c->expert_dtype != MOE_DTYPE_BF16 && c->expert_dtype != MOE_DTYPE_FP4_E2M1)
+    if (c->expert_dtype != MOE_DTYPE_BF16 && c->expert_dtype != MOE_DTYPE_FP4_E2M1 &&
+        c->expert_dtype != MOE_DTYPE_FP8_E4M3_B128)
       return MOE_ERR_INVALID_ARG;
     if (c->dim % 64 != 0 || c->moe_inter_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
   } else {
@@ -55,8 +56,16 @@ int validate(const moe_config *c) {
   if (c->act_quant != MOE_ACT_QUANT_NONE && c->act_quant != MOE_ACT_QUANT_MXFP8)
     return MOE_ERR_INVALID_ARG;
   if (c->act_quant == MOE_ACT_QUANT_MXFP8) {
-    if (c->expert_dtype != MOE_DTYPE_FP4_E2M1) return MOE_ERR_INVALID_ARG;
+    if (c->expert_dtype != MOE_DTYPE_FP4_E2M1 && c->expert_dtype != MOE_DTYPE_FP8_E4M3_B128)
+      return MOE_ERR_INVALID_ARG;
     if (c->dim % 128 != 0 || c->moe_inter_dim % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  }
+  // FP8 (re-dequantised) experts exist only in their own layout and run only
+  // on MXFP8 activations
+  if (c->expert_dtype == MOE_DTYPE_FP8_E4M3_B128) {
+    if (c->act_quant != MOE_ACT_QUANT_MXFP8 || c->weight_layout != MOE_LAYOUT_TILED)
+      return MOE_ERR_INVALID_ARG;
+    if (c->dim > 32768 || c->moe_inter_dim > 32768) return MOE_ERR_UNSUPPORTED;
   }
   if (k > 16 || E > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->route_mode == MOE_ROUTE_HASH) {
@@ -317,7 +326,8 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   if (T == 0) return MOE_OK;
   if (!x || !y || x == y) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
-  if (cfg->expert_dtype == MOE_DTYPE_FP4_E2M1 && (!w->s_gate || !w->s_up || !w->s_down))
+  if ((cfg->expert_dtype == MOE_DTYPE_FP4_E2M1 || cfg->expert_dtype == MOE_DTYPE_FP8_E4M3_B128) &&
+      (!w->s_gate || !w->s_up || !w->s_down))
     return MOE_ERR_INVALID_ARG;
   if (cfg->n_shared_experts == 1 && (!w->sh_gate || !w->sh_up || !w->sh_down))
     return MOE_ERR_INVALID_ARG;
@@ -446,6 +456,18 @@ int moe_pack_weights(const moe_config *cfg, const moe_weights *src, const moe_we
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
+}
+
+int moe_redequant_fp8(const uint8_t *codes, const uint8_t *scales, int64_t n_mat, int32_t N,
+                      int32_t K, uint8_t *fp8, uint8_t *block_scales, uint8_t *lossy,
+                      void *stream) {
+  if (n_mat < 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (N % 128 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (n_mat == 0) return MOE_OK;
+  if (!codes || !scales || !fp8 || !block_scales || !lossy) return MOE_ERR_INVALID_ARG;
+  if (n_mat * (N / 128) * (int64_t)(K / 128) > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_redequant_fp8(codes, scales, n_mat, N, K, fp8, block_scales, lossy,
+                                              (hipStream_t)stream));
 }
 
 int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,

@@ -23,9 +23,16 @@ def cpu_np(t):
     return t.detach().cpu().numpy()
 
 
-def expert_fetcher(layer, cfg):
-    """expert(e) -> float64 (w_gate, w_up, w_down), decoded by the oracle for FP4."""
+def expert_fetcher(layer, cfg, fp8=False):
+    """expert(e) -> float64 (w_gate, w_up, w_down), decoded by the oracle for FP4
+    (fp8: the oracle's FP8 re-dequantisation of the FP4 matrices)."""
     def get(e):
+        if fp8:
+            out = []
+            for n, s in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down")):
+                c, b, _ = oracle.fp4_to_fp8_blocks(cpu_np(layer[n][e]), cpu_np(layer[s][e]))
+                out.append(oracle.fp8_blocks_decode(c, b))
+            return tuple(out)
         if cfg.expert_dtype == "fp4":
             return (oracle.fp4_decode(cpu_np(layer["w_gate"][e]), cpu_np(layer["s_gate"][e])),
                     oracle.fp4_decode(cpu_np(layer["w_up"][e]), cpu_np(layer["s_up"][e])),
@@ -108,12 +115,23 @@ def compare_routing(cfg, gpu_w, gpu_idx, ora_w, ora_idx, aux):
     return differ
 
 
-def oracle_forward(cfg, x, weights, indices, layer):
+def oracle_forward(cfg, x, weights, indices, layer, fp8=False):
     """The oracle layer for cfg: bf16 activations, or MXFP8 activations on the
-    routed FP4 experts."""
+    routed FP4 experts (fp8: on their FP8 re-dequantisation)."""
     f = oracle.layer_forward_mx if cfg.act_quant == "mxfp8" else oracle.layer_forward
-    return f(x, weights, indices, expert_fetcher(layer, cfg), shared_weights(layer, cfg),
+    return f(x, weights, indices, expert_fetcher(layer, cfg, fp8), shared_weights(layer, cfg),
              cfg.swiglu_limit)
+
+
+def run_weights(wl, cfg, layer, B):
+    """(config, layer) the GPU runs for a workload: the FP8 re-dequantisation
+    of an FP4 layer when the workload asks for it (no block may be lossy for
+    the synthetic weights), else the layer as given."""
+    if not wl.fp8_weights:
+        return cfg, layer
+    cfg8, layer8, lossy = B.redequant_layer(cfg, layer)
+    assert lossy == 0
+    return cfg8, layer8
 
 
 def max_rel_err(y, ref):

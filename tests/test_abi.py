@@ -71,6 +71,9 @@ BAD = [
     ("mxfp8 on bf16 experts", replace(V3, act_quant="mxfp8"), B.MOE_ERR_INVALID_ARG),
     ("mxfp8 dim % 128", replace(C.V41_FLASH_FP4_MX.cfg, dim=5120 + 64), B.MOE_ERR_UNSUPPORTED),
     ("mxfp8 inter % 128", replace(C.V41_FLASH_FP4_MX.cfg, moe_inter_dim=1536 + 64), B.MOE_ERR_UNSUPPORTED),
+    ("fp8 experts on bf16 activations", replace(C.V41_FLASH_FP4.cfg, expert_dtype="fp8", weight_layout="tiled"), B.MOE_ERR_INVALID_ARG),
+    ("fp8 experts in the row layout", replace(C.V41_FLASH_FP4_MX.cfg, expert_dtype="fp8"), B.MOE_ERR_INVALID_ARG),
+    ("fp8 experts, dim > 32768", replace(C.V41_FLASH_FP4_MX.cfg, expert_dtype="fp8", weight_layout="tiled", dim=32768 + 128), B.MOE_ERR_UNSUPPORTED),
 ]
 
 
@@ -258,3 +261,21 @@ def test_probes_check_before_any_launch():
     assert B._lib.moe_probe_mfma(0, 0, fake, None, None) == B.MOE_ERR_INVALID_ARG
     assert B._lib.moe_probe_mfma(10, 2, fake, None, None) == B.MOE_ERR_INVALID_ARG
     assert B._lib.moe_probe_mfma(10, 0, None, None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_fp8_expert_config_valid():
+    cfg = replace(C.V41_FLASH_FP4_MX.cfg, expert_dtype="fp8", weight_layout="tiled")
+    assert B.moe_validate_config(cfg) == B.MOE_OK
+
+
+def test_redequant_argument_checks():
+    """Host-side checks of moe_redequant_fp8 (no launch happens)."""
+    fake = ctypes.c_void_p(16)
+    f = B._lib.moe_redequant_fp8
+    assert f(fake, fake, -1, 128, 128, fake, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert f(fake, fake, 1, 0, 128, fake, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert f(fake, fake, 1, 192, 128, fake, fake, fake, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(fake, fake, 1, 128, 64, fake, fake, fake, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(None, fake, 1, 128, 128, fake, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert f(fake, fake, 1, 128, 128, fake, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert f(None, None, 0, 128, 128, None, None, None, None) == B.MOE_OK

@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 # tokens whose output the oracle recomputes (None: all of them)
 SAMPLE = {"tiny_fp32": None, "v3_decode": None, "hash_bf16": 64, "v3_prefill": 24,
-          "v41_flash_fp4": 16, "ngram_bf16": 64, "v41_flash_fp4_mx": 16}
+          "v41_flash_fp4": 16, "ngram_bf16": 64, "v41_flash_fp4_mx": 16, "v41_flash_fp8": 16}
 
 
 def _sample_rows(T, n, seed):
@@ -51,7 +51,10 @@ def test_forward_full_size(name, gpu):
         layer["tid2eid"] = torch.from_numpy(table).to(gpu)
     ws = B.alloc_workspace(cfg, T, gpu)
     y = torch.empty_like(layer["x"])
-    if cfg.act_dtype == "bf16":
+    if wl.fp8_weights:
+        print(f"[full] {name}: re-dequantising the FP4 experts to FP8", flush=True)
+        run_cfg, run_layer = H.run_weights(wl, cfg, layer, B)
+    elif cfg.act_dtype == "bf16":
         print(f"[full] {name}: packing the expert weights", flush=True)
         run_cfg, run_layer = B.pack_layer(cfg, layer)
     else:
@@ -61,7 +64,7 @@ def test_forward_full_size(name, gpu):
     torch.cuda.synchronize()
     v = B.workspace_views(cfg, T, ws)
     assert int(v["flags"][0]) == 0
-    if run_cfg is not cfg:
+    if run_cfg is not cfg and not wl.fp8_weights:
         y_rows = torch.empty_like(y)
         ws_rows = B.alloc_workspace(cfg, T, gpu)
         B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y_rows, ws_rows)
@@ -69,6 +72,8 @@ def test_forward_full_size(name, gpu):
         assert torch.equal(y.view(torch.int16), y_rows.view(torch.int16))
         del y_rows, ws_rows, run_layer
 
+    if wl.fp8_weights:
+        del run_layer
     # routing of every token
     print(f"[full] {name}: oracle routing", flush=True)
     ow, oidx, aux = H.oracle_route(cfg, layer, ora_table)
@@ -94,7 +99,7 @@ def test_forward_full_size(name, gpu):
     rows = rows[~differ[rows]]
     print(f"[full] {name}: oracle forward of {rows.size} tokens", flush=True)
     x_rows = H.f64(layer["x"][torch.as_tensor(rows, device=gpu)])
-    yref = H.oracle_forward(cfg, x_rows, ow[rows], oidx[rows], layer)
+    yref = H.oracle_forward(cfg, x_rows, ow[rows], oidx[rows], layer, fp8=wl.fp8_weights)
     ygpu = H.f64(y[torch.as_tensor(rows, device=gpu)])
     err = H.max_rel_err(ygpu, yref)
     tol = H.TOL[cfg.expert_dtype if cfg.expert_dtype == "fp4" else cfg.act_dtype]

@@ -35,11 +35,15 @@ def _layer(workload, device):
     return layer, ora_table
 
 
-def _forward(workload, layer, device):
+def _forward(workload, layer, device, as_run=False):
+    """moe_forward of the workload's layer (as_run: on the weights the workload
+    runs with, i.e. FP8 re-dequantised ones where it asks for them)."""
     cfg, T = workload.cfg, workload.T
+    if as_run:
+        cfg, layer = H.run_weights(workload, cfg, layer, B)
     ws = B.alloc_workspace(cfg, T, device)
     y = torch.empty_like(layer["x"])
-    print(f"[forward] {workload.name} T={T}", flush=True)
+    print(f"[forward] {workload.name} T={T} ({cfg.expert_dtype} experts)", flush=True)
     B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y, ws)
     torch.cuda.synchronize()
     return y, ws
@@ -119,7 +123,7 @@ def test_forward_small(name, gpu):
     wl = C.SMALL_WORKLOADS[name]
     cfg, T = wl.cfg, wl.T
     layer, ora_table = _layer(wl, gpu)
-    y, ws = _forward(wl, layer, gpu)
+    y, ws = _forward(wl, layer, gpu, as_run=True)
     v = B.workspace_views(cfg, T, ws)
     ow, oidx, aux = H.oracle_route(cfg, layer, ora_table)
     gidx = H.cpu_np(v["route_indices"])
@@ -133,7 +137,8 @@ def test_forward_small(name, gpu):
         np.testing.assert_array_equal(st[:T * cfg.n_activated_experts], ost)
         np.testing.assert_array_equal(inv, oinv)
     keep = ~differ
-    yref = H.oracle_forward(cfg, H.f64(layer["x"])[keep], ow[keep], oidx[keep], layer)
+    yref = H.oracle_forward(cfg, H.f64(layer["x"])[keep], ow[keep], oidx[keep], layer,
+                            fp8=wl.fp8_weights)
     err = H.max_rel_err(H.f64(y)[keep], yref)
     print(f"[forward] {name}: max rel err {err:.3e}", flush=True)
     assert err <= H.TOL[cfg.expert_dtype if cfg.expert_dtype == "fp4" else cfg.act_dtype]
