@@ -1,5 +1,5 @@
-// FP4 experts on MXFP8 activations for gfx950: the activation quantiser and
-// the grouped GEMM tile on v_mfma_scale_f32_16x16x128_f8f6f4.
+// Routed experts on MXFP8 activations for gfx950: the activation quantiser and
+// the grouped GEMMs on v_mfma_scale_f32_16x16x128_f8f6f4.
 //
 // "From One Giant FFN to 384 Tiny Experts", Ch.11.6: the experts are stored
 // as FP4 (E2M1) in OCP MXFP4 1x32 sub-blocks and computed in FP8 (E4M3).  On
@@ -10,14 +10,23 @@
 // columns x 128 inputs.  Operand layout (lane l, r = l % 16, q = l / 16):
 //   A (E4M3, 32 bytes): row r, inputs 16q .. 16q+15 and 64+16q .. 64+16q+15
 //   B (E2M1, 16 bytes): column r, inputs 32q .. 32q+31 (low nibble first)
+//   B (E4M3, 32 bytes): column r, inputs as A's
 //   scales: lane l gives the E8M0 scale of its row (A) / column (B) for the
 //           32-input block q
 //   D: column r, rows 4q .. 4q+3 (as the 16x16x32 form)
 //
-// The pipeline is the one of the bf16 tile (experts.hip): 128-input stages
-// now, activation rows (one 128-byte line per row and stage) and their scale
-// words copied global -> LDS, FP4 codes and scales into a register ring,
-// static waits, refills spread over the MFMA chunks.
+// Two grouped-GEMM forms:
+//   grouped_gemm_mx     decode tiles (one 16-row block), FP4 weights: the
+//                       pipeline of the bf16 tile (experts.hip) with 128-input
+//                       stages -- activation rows and their scale words
+//                       copied global -> LDS and read by every wave, FP4 codes
+//                       and scales in a register ring, the waves splitting the
+//                       columns;
+//   grouped_gemm_mx_rs  tiles of 4 and more row blocks, and every FP8-weight
+//                       tile: the waves split the rows and the weights pass
+//                       through LDS (gemm_tile_mx_rs below); FP4 weights as
+//                       stored or FP8 weights re-dequantised from them
+//                       (redequant.hip).
 
 #include "fp8.h"
 #include "gemm.h"
@@ -66,8 +75,8 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const bf16 *src, in
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// One tile on the scaled MFMA: MBE 16-row blocks, NB weight matrices, NCB
-// 16-column blocks per wave and matrix.  SLOT = bytes per LDS ring slot
+// One decode tile on the scaled MFMA: MBE 16-row blocks, NB weight matrices,
+// NCB 16-column blocks per wave and matrix.  SLOT = bytes per LDS ring slot
 // (activation units, then the scale region).
 template <int WAVES, int NB, int NCB, int MBE, int NS, int SLOT>
 __device__ __forceinline__ void gemm_tile_mx(const GemmArgs &g, const TileCtx &t, uint8_t *Ls) {
@@ -678,30 +687,18 @@ constexpr int gemm_mx_slot_bytes() {
   return NFW * WAVES * 1024 + NSW * WAVES * 256;
 }
 
-// WPE: waves per SIMD the kernel is compiled for (2: 256 registers per wave;
-// 1: 512, for the tall tiles whose accumulators would otherwise spill).
+// Decode-tile kernel.  WPE: waves per SIMD it is compiled for (2: 256
+// registers per wave; 1: 512).
 template <int WAVES, int NB, int NCB, int MB, int NS, int WPE>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void grouped_gemm_mx(const GemmArgs g) {
+  static_assert(MB < MCH, "tiles of 4+ row blocks run in grouped_gemm_mx_rs");
   constexpr int SLOT = gemm_mx_slot_bytes<WAVES, NB, NCB, MB, NS>();
   __shared__ __attribute__((aligned(1024))) uint8_t Ls[NS * SLOT];
   int tile, slab;
   if (!gemm_work_item(g, &tile, &slab)) return;
   const TileCtx t = gemm_tile_ctx(g, tile, slab, WAVES, NCB * 16);
-  const int nmb = (t.rows + 15) >> 4;
-  if constexpr (MB < MCH) {
-    gemm_tile_mx<WAVES, NB, NCB, MB, NS, SLOT>(g, t, Ls);
-  } else {
-    const int nch = (nmb + MCH - 1) / MCH;
-    if (nch <= 1 || MB < 2 * MCH)
-      gemm_tile_mx<WAVES, NB, NCB, (MB < MCH ? MB : MCH), NS, SLOT>(g, t, Ls);
-    else if (nch == 2 || MB < 3 * MCH)
-      gemm_tile_mx<WAVES, NB, NCB, (MB < 2 * MCH ? MB : 2 * MCH), NS, SLOT>(g, t, Ls);
-    else if (nch == 3 || MB < 4 * MCH)
-      gemm_tile_mx<WAVES, NB, NCB, (MB < 3 * MCH ? MB : 3 * MCH), NS, SLOT>(g, t, Ls);
-    else
-      gemm_tile_mx<WAVES, NB, NCB, MB, NS, SLOT>(g, t, Ls);
-  }
+  gemm_tile_mx<WAVES, NB, NCB, MB, NS, SLOT>(g, t, Ls);
 }
 
 template <int WAVES, int NB, int NCB, int MB, int NS, int WPE>
@@ -714,8 +711,8 @@ hipError_t run_gemm_mx(GemmArgs a, int max_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Decode tiles (one row block): 8 waves splitting the columns.  Tiles of 4+
-// row blocks: the row-split kernel, 4 waves with the whole register file.
+// FP4 decode tiles (one row block): 8 waves splitting the columns.  Tiles of
+// 4+ row blocks: the row-split kernel, 4 waves with the whole register file.
 // Every slab re-reads the tile's activations, so the slabs are as wide as the
 // accumulators allow: for tiles of up to 12 row blocks 128 columns of gate and
 // of up, or 256 down columns (half that when the width does not divide).
