@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(REPO_DIR, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "experts.hip", "pack.hip", "probe.hip", "experts_mx.hip", "redequant.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "experts.hip", "pack.hip", "probe.hip", "experts_mx.hip", "redequant.hip", "dense.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [

@@ -184,6 +184,11 @@ SMALL_WORKLOADS = {
         "dense_router_ragged",
         replace(V3_PREFILL.cfg, dim=512, moe_inter_dim=128, n_routed_experts=64),
         T=1100, description="1024+ tokens: GEMM-kernel router (last tile 12 rows), chunked permute"),
+    "dense32_router": Workload(
+        "dense32_router",
+        replace(V3_PREFILL.cfg, dim=1024, moe_inter_dim=128),
+        T=1030, description="1024+ tokens, 256 experts: 32x32x16 score GEMM split 4 ways over "
+                            "the inputs (last row tile 6 rows)"),
     "split_router_e48": Workload(
         "split_router_e48",
         MoEConfig(dim=256, n_routed_experts=48, n_activated_experts=6, moe_inter_dim=128,

@@ -623,8 +623,18 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   a.SB[0] = (const bf16 *)w.sh_gate; a.SB[1] = (const bf16 *)w.sh_up;
   a.C = (bf16 *)p.h;
   a.limit = p.swiglu_limit;
+  // the shared expert of FP4 layers runs as launches of its own; its gate|up
+  // GEMM on the dense 32x32x16 kernel where the widths allow (rows
+  // routed_rows .. of H).  Its down GEMM stays on the grouped kernel, whose
+  // 192 x 256 tiles read less per MFMA than the dense kernel's 128 x 128.
+  const bool dense_shared = p.inter % 128 == 0 && p.dim % 128 == 0;
   if (fp4) {
-    if (p.n_shared_tiles > 0) {
+    if (p.n_shared_tiles > 0 && dense_shared) {
+      if ((err = launch_dense_swiglu(p.x, p.T, p.dim, p.inter, w.sh_gate, w.sh_up, p.tiled,
+                                     p.swiglu_limit, (bf16 *)p.h + routed_rows * p.inter, s)) !=
+          hipSuccess)
+        return err;
+    } else if (p.n_shared_tiles > 0) {
       GemmArgs sh = a;
       sh.tile_begin = 0; sh.tile_end = p.n_shared_tiles;
       if ((err = gemm_launch(2, false, mb, sh, p.n_shared_tiles, s)) != hipSuccess) return err;

@@ -21,6 +21,15 @@ size_t route_logits_floats(const moe_config &cfg, int64_t T);
 hipError_t launch_dense_logits(const void *x, const void *w, int64_t T, int d, int E, float *z,
                                hipStream_t s);
 
+// Dense bf16 GEMMs on the 32x32x16 MFMA (dense.hip); N % 128 == 0, K % 64 == 0.
+//   swiglu:    H[M, N] = SwiGLU(A Bg^T, A Bu^T) (clamped at `limit` > 0), bf16
+//   f32_parts: Cf[p, M, N] = A[:, Kp] B[:, Kp]^T for the k_parts splits Kp of K
+// B matrices [N, K] in the row layout or (`tiled`) the moe_pack_weights one.
+hipError_t launch_dense_swiglu(const void *A, int64_t M, int K, int N, const void *Bg,
+                               const void *Bu, bool tiled, float limit, void *H, hipStream_t s);
+hipError_t launch_dense_f32_parts(const void *A, int64_t M, int K, int N, const void *B,
+                                  int k_parts, float *Cf, hipStream_t s);
+
 // 2-gram hash routing: pairs [T, 2] (previous id, current id); primes
 // [k] the k smallest primes above cfg.vocab_size.
 hipError_t launch_route_ngram(const moe_config &cfg, const int32_t *pairs, const int64_t *primes,

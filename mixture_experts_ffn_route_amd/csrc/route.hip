@@ -331,6 +331,17 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, co
 // waves); small ones use route_logits_bf16 split over the input dimension.
 static bool use_dense_logits(int64_t T, int E) { return T >= 1024 && E % 64 == 0; }
 
+// Splits of the input dimension for the 32x32x16 dense score GEMM (E % 128 ==
+// 0): enough (row tile, expert tile, split) items to cover the GPU twice, each
+// split at least 4 stages of 64 inputs; 0 when the dense GEMM does not apply.
+static int dense32_parts(int64_t T, int E, int d) {
+  if (E % 128 != 0 || d % 64 != 0) return 0;
+  const int64_t items = ((T + 127) / 128) * (E / 128);
+  int kp = 1;
+  while (kp < 8 && items * kp < 512 && d / 64 >= 8 * kp) kp *= 2;
+  return kp;
+}
+
 // Split-router shape for T tokens: row blocks per workgroup and input parts.
 static void split_shape(int64_t T, int E, int d, int *mt, int *ks) {
   *mt = T >= 1024 ? 4 : 1;
@@ -342,7 +353,10 @@ static void split_shape(int64_t T, int E, int d, int *mt, int *ks) {
 
 size_t route_logits_floats(const moe_config &cfg, int64_t T) {
   if (cfg.route_mode != MOE_ROUTE_LEARNED || cfg.act_dtype != MOE_DTYPE_BF16) return 0;
-  if (use_dense_logits(T, cfg.n_routed_experts)) return (size_t)T * cfg.n_routed_experts;
+  if (use_dense_logits(T, cfg.n_routed_experts)) {
+    const int kp = dense32_parts(T, cfg.n_routed_experts, cfg.dim);
+    return (size_t)(kp > 0 ? kp : 1) * T * cfg.n_routed_experts;
+  }
   int mt, ks;
   split_shape(T, cfg.n_routed_experts, cfg.dim, &mt, &ks);
   return (size_t)ks * T * cfg.n_routed_experts;
@@ -512,10 +526,14 @@ static hipError_t launch_learned_epl(const RouteArgs &a, int act_dtype, hipStrea
 template <int EPL>
 static hipError_t launch_split_epl(const RouteArgs &a, float *zpart, hipStream_t s) {
   if (use_dense_logits(a.T, a.E)) {
-    const hipError_t e = launch_dense_logits(a.x, a.w, a.T, a.d, a.E, zpart, s);
+    // experts in multiples of 128: the 32x32x16 GEMM, the input dimension
+    // split into kp parts that the selection kernel adds in order
+    const int kp = dense32_parts(a.T, a.E, a.d);
+    const hipError_t e = kp > 0 ? launch_dense_f32_parts(a.x, a.T, a.d, a.E, a.w, kp, zpart, s)
+                                : launch_dense_logits(a.x, a.w, a.T, a.d, a.E, zpart, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(route_select_kernel<EPL>, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0,
-                       s, a, (const float *)zpart, 1);
+                       s, a, (const float *)zpart, kp > 0 ? kp : 1);
     return hipGetLastError();
   }
   int mt, ks;
