@@ -326,9 +326,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(const RouteArgs a, co
   if (t < a.T) select_token<EPL>(a, zpart + t * a.E, t, lane, KS, a.T * (int64_t)a.E);
 }
 
-// Large batches with E % 64 == 0 compute the logits on the grouped-GEMM
-// kernel (activation rows copied to LDS as whole lines and shared by the four
-// waves); small ones use route_logits_bf16 split over the input dimension.
+// Large batches with E % 64 == 0 compute the logits on a GEMM kernel: the
+// dense 32x32x16 one split over the input dimension when E % 128 == 0, else
+// the grouped-GEMM kernel as one group; small batches use route_logits_bf16
+// split over the input dimension.
 static bool use_dense_logits(int64_t T, int E) { return T >= 1024 && E % 64 == 0; }
 
 // Splits of the input dimension for the 32x32x16 dense score GEMM (E % 128 ==
