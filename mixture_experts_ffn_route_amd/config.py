@@ -194,6 +194,17 @@ SMALL_WORKLOADS = {
         MoEConfig(dim=256, n_routed_experts=48, n_activated_experts=6, moe_inter_dim=128,
                   score_func="sigmoid", route_scale=1.0, has_bias=True),
         T=1030, description="1024+ tokens with E % 64 != 0: split router, chunked permute"),
+    "v3_narrow_2050": Workload(
+        "v3_narrow_2050",
+        replace(V3_PREFILL.cfg, dim=256, moe_inter_dim=128, n_routed_experts=64),
+        T=2050, description="2048+ tokens at narrow widths: many chunks in the permutation, "
+                            "ragged last row tile of the score GEMM"),
+    "noshared_2051": Workload(
+        "noshared_2051",
+        MoEConfig(dim=192, n_routed_experts=16, n_activated_experts=3, moe_inter_dim=128,
+                  n_shared_experts=0, score_func="sigmoid", route_scale=1.0, has_bias=True),
+        T=2051, description="2048+ tokens, no shared expert, width 192 (a combine lane "
+                            "group of 256 covers less than one row)"),
     # limits and degenerate cases
     "max_e512_k16": Workload(
         "max_e512_k16",

@@ -205,8 +205,12 @@ __device__ __forceinline__ void dense_tile(const DenseArgs &g, int64_t m0, int n
 
 // Items (row tile, column tile, K part) are dealt to the 8 XCDs in contiguous
 // runs, column tiles fastest, so the column tiles of one row tile share an L2.
+// The one-matrix form (router scores: short K parts, latency-bound) runs a
+// 2-stage ring in 64 KB of LDS so that two workgroups share a CU and cover
+// each other's waits; the two-matrix form keeps one workgroup per CU.
 template <int NB, int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1,
+                                                                     NB == 1 ? 2 : 1)))
 void dense_gemm(const DenseArgs g) {
   constexpr int SLOT = (16 + NB * 16) * 1024;
   __shared__ __attribute__((aligned(1024))) uint8_t L0[SLOT];
@@ -255,7 +259,7 @@ hipError_t launch_dense_f32_parts(const void *A, int64_t M, int K, int N, const 
   g.A = (const bf16 *)A; g.M = M; g.K = K; g.N = N;
   g.B[0] = (const bf16 *)B;
   g.tiled = 0; g.k_parts = k_parts; g.Cf = Cf;
-  return run_dense<1, 3>(g, s);
+  return run_dense<1, 2>(g, s);
 }
 
 }  // namespace moe

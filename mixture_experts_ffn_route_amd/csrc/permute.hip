@@ -204,22 +204,36 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(const PermuteAr
   extern __shared__ int tot[];                  // [E] pairs per expert, then scratch
   int *scratch = tot + a.E;                     // [kPermWaves + 1]
   const int E = a.E, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int e = w; e < E; e += kPermWaves) {
-    int32_t *col = chist + (int64_t)e * C;
-    int carry = 0;
+  // Each wave scans kScanGroup experts side by side, so their loads are in
+  // flight together instead of one expert's load-scan-store after another.
+  constexpr int kScanGroup = 8;
+  for (int e0 = w * kScanGroup; e0 < E; e0 += kPermWaves * kScanGroup) {
+    int carry[kScanGroup];
+#pragma unroll
+    for (int j = 0; j < kScanGroup; ++j) carry[j] = 0;
     for (int c0 = 0; c0 < C; c0 += 64) {
       const int c = c0 + lane;
-      const int v = c < C ? col[c] : 0;
-      int inc = v;
+      int v[kScanGroup];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(inc, off);
-        if (lane >= off) inc += o;
+      for (int j = 0; j < kScanGroup; ++j)
+        v[j] = (c < C && e0 + j < E) ? chist[(int64_t)(e0 + j) * C + c] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanGroup; ++j) {
+        int inc = v[j];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(inc, off);
+          if (lane >= off) inc += o;
+        }
+        if (c < C && e0 + j < E) chist[(int64_t)(e0 + j) * C + c] = carry[j] + inc - v[j];
+        carry[j] += __shfl(inc, 63);
       }
-      if (c < C) col[c] = carry + inc - v;
-      carry += __shfl(inc, 63);
     }
-    if (lane == 0) tot[e] = carry;
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < kScanGroup; ++j)
+        if (e0 + j < E) tot[e0 + j] = carry[j];
+    }
   }
   __syncthreads();
   int carry_rows = 0, carry_tiles = 0;

@@ -44,12 +44,18 @@ __device__ __forceinline__ void select_token(const RouteArgs &a, const float *zr
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane * EPL + j;
-    float z = -INFINITY;
-    if (e < E) {
-      z = zrow[e];
-      for (int q = 1; q < nparts; ++q) z += zrow[q * pstride + e];
+    s[j] = e < E ? zrow[e] : -INFINITY;
+  }
+  // parts added in order; each part's EPL loads are issued together
+  for (int q = 1; q < nparts; ++q) {
+    float v[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane * EPL + j;
+      v[j] = e < E ? zrow[q * pstride + e] : 0.f;
     }
-    s[j] = z;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) s[j] += v[j];
   }
   // affinity
   if (a.score_func == MOE_SCORE_SOFTMAX) {
