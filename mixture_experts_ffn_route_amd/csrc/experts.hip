@@ -67,21 +67,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
   const int lane = t.lane, wave = t.wave, r16 = lane & 15, jq = lane >> 4;
   const int K = t.K, N = t.N, rows = t.rows, row0 = t.row0, col0 = t.col0;
 
-  // down GEMM: gate value of each output row this lane stores (rows
-  // 16m + 4jq + i), loaded up front so the latency hides under the main loop.
-  // (The LDS holds nothing but the copy ring: with a second LDS object the
-  // compiler adds a full vmcnt drain before every LDS read.)
-  float row_w[NB == 1 ? MBE : 1][4];
+  // down GEMM: thread `tid` loads the gate value of tile row tid up front (the
+  // latency hides under the main loop) and holds it in one register; the
+  // epilogue shares the values through the drained copy ring.  (The LDS holds
+  // nothing but the ring: with a second LDS object the compiler adds a full
+  // vmcnt drain before every LDS read.)
+  static_assert(NB != 1 || 16 * MBE <= WAVES * 64, "one row per thread");
+  const int tid = wave * 64 + lane;
+  float my_w = 1.f;
   if constexpr (NB == 1) {
-#pragma unroll
-    for (int m = 0; m < MBE; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int r = m * 16 + jq * 4 + i;
-        r = r < rows ? r : rows - 1;
-        const int64_t R = row0 + r;
-        row_w[m][i] = R < g.routed_rows ? g.sorted_w[R < g.routed_rows ? R : 0] : 1.f;
-      }
+    const int64_t R = row0 + tid;
+    if (tid < rows && R < g.routed_rows) my_w = g.sorted_w[R];
   }
 
   // ---- activation copies.  A stage holds, per 16-row block m, two 1 KB
@@ -282,6 +278,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
         }
       }
   } else {
+    // every wave has read its last stage (barrier), then the ring's first
+    // floats take the row gate values
+    float *rw = (float *)As;
+    __syncthreads();
+    if (tid < 16 * MBE) rw[tid] = my_w;
+    __syncthreads();
 #pragma unroll
     for (int m = 0; m < MBE; ++m)
 #pragma unroll
@@ -289,12 +291,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
         const int row = m * 16 + jq * 4 + i;
         if (row < rows) {
           const int64_t o = (int64_t)(row0 + row) * N + col0 + r16;
+          const float w = rw[row];
           if (g.Cf) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) g.Cf[o + cb * 16] = acc[m][0][cb][i] * row_w[m][i];
+            for (int cb = 0; cb < NCB; ++cb) g.Cf[o + cb * 16] = acc[m][0][cb][i] * w;
           } else {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) g.C[o + cb * 16] = (bf16)(acc[m][0][cb][i] * row_w[m][i]);
+            for (int cb = 0; cb < NCB; ++cb) g.C[o + cb * 16] = (bf16)(acc[m][0][cb][i] * w);
           }
         }
       }
