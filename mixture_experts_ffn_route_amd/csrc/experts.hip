@@ -67,17 +67,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
   const int lane = t.lane, wave = t.wave, r16 = lane & 15, jq = lane >> 4;
   const int K = t.K, N = t.N, rows = t.rows, row0 = t.row0, col0 = t.col0;
 
-  // down GEMM: thread `tid` loads the gate value of tile row tid up front (the
-  // latency hides under the main loop) and holds it in one register; the
-  // epilogue shares the values through the drained copy ring.  (The LDS holds
-  // nothing but the ring: with a second LDS object the compiler adds a full
-  // vmcnt drain before every LDS read.)
-  static_assert(NB != 1 || 16 * MBE <= WAVES * 64, "one row per thread");
-  const int tid = wave * 64 + lane;
-  float my_w = 1.f;
-  if constexpr (NB == 1) {
-    const int64_t R = row0 + tid;
-    if (tid < rows && R < g.routed_rows) my_w = g.sorted_w[R];
+  // down GEMM: the gate values of the tile's rows, loaded up front (the latency
+  // hides under the main loop) and spread over the wave, lane l holding rows
+  // l, l + 64, ...; the epilogue fetches each stored row's value by a lane
+  // shuffle.  NWR registers instead of one per stored row (4 MBE).
+  constexpr int NWR = NB == 1 ? (16 * MBE + 63) / 64 : 1;
+  float my_w[NWR];
+#pragma unroll
+  for (int j = 0; j < NWR; ++j) {
+    const int r = 64 * j + lane;
+    const int64_t R = row0 + r;
+    my_w[j] = (NB == 1 && r < rows && R < g.routed_rows) ? g.sorted_w[R] : 1.f;
   }
 
   // ---- activation copies.  A stage holds, per 16-row block m, two 1 KB
@@ -278,20 +278,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
         }
       }
   } else {
-    // every wave has read its last stage (barrier), then the ring's first
-    // floats take the row gate values
-    float *rw = (float *)As;
-    __syncthreads();
-    if (tid < 16 * MBE) rw[tid] = my_w;
-    __syncthreads();
 #pragma unroll
     for (int m = 0; m < MBE; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + jq * 4 + i;
+        // row / 64 = m / 4 for every lane; every lane takes part in the shuffle
+        const float w = __shfl(my_w[m >> 2], row & 63);
         if (row < rows) {
           const int64_t o = (int64_t)(row0 + row) * N + col0 + r16;
-          const float w = rw[row];
           if (g.Cf) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) g.Cf[o + cb * 16] = acc[m][0][cb][i] * w;

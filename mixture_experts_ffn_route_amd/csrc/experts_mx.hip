@@ -367,17 +367,14 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
   const int mb0 = wave * MW;
   const bool tiled = g.tiled != 0;
 
-  float row_w[NB == 1 ? MW : 1][4];
+  // down GEMM: lane l holds the gate value of this wave's row l (a wave owns
+  // at most 64 rows); the epilogue fetches each stored row's value by a lane
+  // shuffle, so the main loop keeps one register for them.
+  float my_w = 1.f;
   if constexpr (NB == 1) {
-#pragma unroll
-    for (int m = 0; m < MW; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int r = (mb0 + m) * 16 + q * 4 + i;
-        r = r < rows ? r : rows - 1;
-        const int64_t R = row0 + r;
-        row_w[m][i] = R < g.routed_rows ? g.sorted_w[R < g.routed_rows ? R : 0] : 1.f;
-      }
+    const int r = mb0 * 16 + lane;
+    const int64_t R = row0 + r;
+    if (lane < MW * 16 && r < rows && R < g.routed_rows) my_w = g.sorted_w[R];
   }
 
   // activation copies of this wave: unit (m, h) = rows 16(mb0+m) + 8h .. +7
@@ -610,11 +607,12 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
     for (int m = 0; m < MW; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const float w = __shfl(my_w, m * 16 + q * 4 + i);   // every lane takes part
         const int row = (mb0 + m) * 16 + q * 4 + i;
         if (row < rows) {
           bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
 #pragma unroll
-          for (int cb = 0; cb < SC; ++cb) crow[cb * 16] = (bf16)(acc[m][0][cb][i] * row_w[m][i]);
+          for (int cb = 0; cb < SC; ++cb) crow[cb * 16] = (bf16)(acc[m][0][cb][i] * w);
         }
       }
   }
