@@ -4,12 +4,16 @@
 A step is one full forward of the layer (route -> permute -> grouped GEMM1
 with SwiGLU -> grouped GEMM2 -> combine with the shared expert) over one
 batch of synthetic tokens, through the C ABI (moe_forward_profiled).  Inputs
-and weights are resident in HBM before the timed region starts.
+and weights are resident in HBM before the timed region starts.  For FP4 /
+FP8 expert layers the library runs the shared expert on a side stream during
+routing; the step time covers it (the combine waits for it), the stage times
+do not.
 
 Prints one JSON line:
   value        tokens/s of the DeepSeek-V3-shaped prefill layer (T=4096)
-  roofline     the dominant kernel (grouped GEMM1: gate|up + SwiGLU) against
-               its bound, timed with HIP events on the library's stream
+  roofline     the dominant kernel (grouped GEMM1: gate|up + SwiGLU; the
+               routed experts' launch for FP4 / FP8 layers) against its
+               bound, timed with HIP events on the library's stream
   cpu_baseline the float64 CPU oracle on a bounded sample of the same batch
   decode       the T=64 decode layer of the same weights (tokens/s, GB/s)
 """
@@ -78,8 +82,11 @@ def algorithmic_counts(wl, counts):
     n_hit = int((counts > 0).sum())
     sh = cfg.n_shared_experts
     rows = T * k + T * sh
-    gemm1 = {"flops": 4.0 * d * I * rows,
-             "bytes": n_hit * 2 * mat + sh * 2 * I * d * eb + T * d * eb}
+    # the up-GEMM stage: FP4 / FP8 expert layers run the shared expert on the
+    # library's side stream, concurrently with the routing, outside the stage
+    sh1 = 0 if (cfg.act_dtype == "bf16" and (cfg.expert_dtype == "fp4" or wl.fp8_weights)) else sh
+    gemm1 = {"flops": 4.0 * d * I * (T * k + T * sh1),
+             "bytes": n_hit * 2 * mat + sh1 * 2 * I * d * eb + T * d * eb}
     layer_flops = 6.0 * d * I * rows + (2.0 * T * d * E if cfg.route_mode == "learned" else 0.0)
     layer_bytes = n_hit * 3 * mat + sh * 3 * I * d * eb + 2 * T * d * eb
     layer_bytes += (E * d * eb + 4 * E) if cfg.route_mode == "learned" else 4 * T * k

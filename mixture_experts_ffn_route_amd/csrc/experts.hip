@@ -568,6 +568,59 @@ static hipError_t mark(const ExpertPlan &p, int i, hipStream_t s) {
   return p.events ? hipEventRecord(p.events[i], s) : hipSuccess;
 }
 
+// The shared expert on the grouped kernel's dense form: its rows in order (no
+// tile list), group 0 taken as the shared group (E = 0) and every row's gate
+// value 1 (no row is below routed_rows = 0).
+static GemmArgs shared_dense_args(const ExpertPlan &p, int tile_rows) {
+  GemmArgs a = {};
+  a.E = 0;
+  a.routed_rows = 0;
+  a.tiled = p.tiled ? 1 : 0;
+  a.dense_rows = p.T;
+  a.dense_tile_rows = tile_rows;
+  a.tile_begin = 0;
+  a.tile_end = (int)((p.T + tile_rows - 1) / tile_rows);
+  return a;
+}
+
+hipError_t launch_shared_expert(const ExpertPlan &p, hipStream_t s, hipEvent_t xq_ready) {
+  hipError_t err;
+  const int64_t routed_rows = p.T * p.k;
+  const moe_weights &w = *p.w;
+  if (p.mx) {
+    if ((err = launch_quantize_mxfp8((const bf16 *)p.x, p.T, p.dim, p.xq, p.xq_scales, s)) !=
+        hipSuccess)
+      return err;
+    if ((err = hipEventRecord(xq_ready, s)) != hipSuccess) return err;
+  }
+  if (!p.has_shared) return hipSuccess;
+  bf16 *hs = (bf16 *)p.h + routed_rows * p.inter;
+  const int mb = p.tile_rows / 16;
+  // gate|up + SwiGLU: the dense 32x32x16 kernel where the widths allow
+  if (p.inter % 128 == 0 && p.dim % 128 == 0) {
+    if ((err = launch_dense_swiglu(p.x, p.T, p.dim, p.inter, w.sh_gate, w.sh_up, p.tiled,
+                                   p.swiglu_limit, hs, s)) != hipSuccess)
+      return err;
+  } else {
+    GemmArgs a = shared_dense_args(p, p.tile_rows);
+    a.A = (const bf16 *)p.x;
+    a.K = p.dim;
+    a.N = p.inter;
+    a.SB[0] = (const bf16 *)w.sh_gate; a.SB[1] = (const bf16 *)w.sh_up;
+    a.C = hs;
+    a.limit = p.swiglu_limit;
+    if ((err = gemm_launch(2, false, mb, a, a.tile_end, s)) != hipSuccess) return err;
+  }
+  // down projection on the grouped kernel (its tiles read less per MFMA here)
+  GemmArgs a = shared_dense_args(p, p.tile_rows);
+  a.A = hs;
+  a.K = p.inter;
+  a.N = p.dim;
+  a.SB[0] = (const bf16 *)w.sh_down;
+  a.C = (bf16 *)p.yrows + routed_rows * p.dim;
+  return gemm_launch(1, false, mb, a, a.tile_end, s);
+}
+
 hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   const int64_t routed_rows = p.T * p.k;
   const int64_t total_rows = routed_rows + (p.has_shared ? p.T : 0);
@@ -621,13 +674,18 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   a.SB[0] = (const bf16 *)w.sh_gate; a.SB[1] = (const bf16 *)w.sh_up;
   a.C = (bf16 *)p.h;
   a.limit = p.swiglu_limit;
-  // the shared expert of FP4 layers runs as launches of its own; its gate|up
-  // GEMM on the dense 32x32x16 kernel where the widths allow (rows
-  // routed_rows .. of H).  Its down GEMM stays on the grouped kernel, whose
-  // 192 x 256 tiles read less per MFMA than the dense kernel's 128 x 128.
+  // With a side stream the shared expert is already launched there and the
+  // launches below cover the routed tiles only.  Otherwise the shared expert
+  // of FP4 layers runs as launches of its own; its gate|up GEMM on the dense
+  // 32x32x16 kernel where the widths allow (rows routed_rows .. of H).  Its
+  // down GEMM stays on the grouped kernel, whose 192 x 256 tiles read less per
+  // MFMA than the dense kernel's 128 x 128.
+  const bool side = p.shared_done != nullptr;
   const bool dense_shared = p.inter % 128 == 0 && p.dim % 128 == 0;
-  if (fp4) {
-    if (p.n_shared_tiles > 0 && dense_shared) {
+  if (fp4 || side) {
+    if (side) {
+      if (p.mx && (err = hipStreamWaitEvent(s, p.xq_ready, 0)) != hipSuccess) return err;
+    } else if (p.n_shared_tiles > 0 && dense_shared) {
       if ((err = launch_dense_swiglu(p.x, p.T, p.dim, p.inter, w.sh_gate, w.sh_up, p.tiled,
                                      p.swiglu_limit, (bf16 *)p.h + routed_rows * p.inter, s)) !=
           hipSuccess)
@@ -640,14 +698,14 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
     a.tile_begin = p.n_shared_tiles; a.tile_end = -1;
     if (p.mx) {
       // routed experts on MXFP8 activations: quantise x, gather its rows
-      if ((err = launch_quantize_mxfp8((const bf16 *)p.x, p.T, p.dim, p.xq, p.xq_scales, s)) !=
-          hipSuccess)
+      if (!side && (err = launch_quantize_mxfp8((const bf16 *)p.x, p.T, p.dim, p.xq,
+                                                p.xq_scales, s)) != hipSuccess)
         return err;
       a.Aq = p.xq;
       a.Asc = p.xq_scales;
       if ((err = launch_gemm_mx(2, mb, a, p.max_tiles - p.n_shared_tiles, s)) != hipSuccess)
         return err;
-    } else if ((err = gemm_launch(2, true, mb, a, p.max_tiles - p.n_shared_tiles, s)) !=
+    } else if ((err = gemm_launch(2, fp4, mb, a, p.max_tiles - p.n_shared_tiles, s)) !=
                hipSuccess) {
       return err;
     }
@@ -667,8 +725,8 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   a.S[0] = w.s_down; a.S[1] = nullptr;
   a.SB[0] = (const bf16 *)w.sh_down; a.SB[1] = nullptr;
   a.C = (bf16 *)p.yrows;
-  if (fp4) {
-    if (p.n_shared_tiles > 0) {
+  if (fp4 || side) {
+    if (!side && p.n_shared_tiles > 0) {
       GemmArgs sh = a;
       sh.tile_begin = 0; sh.tile_end = p.n_shared_tiles;
       if ((err = gemm_launch(1, false, mb, sh, p.n_shared_tiles, s)) != hipSuccess) return err;
@@ -683,7 +741,7 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
       a.Asc = p.hq_scales;
       if ((err = launch_gemm_mx(1, mb, a, p.max_tiles - p.n_shared_tiles, s)) != hipSuccess)
         return err;
-    } else if ((err = gemm_launch(1, true, mb, a, p.max_tiles - p.n_shared_tiles, s)) !=
+    } else if ((err = gemm_launch(1, fp4, mb, a, p.max_tiles - p.n_shared_tiles, s)) !=
                hipSuccess) {
       return err;
     }
@@ -694,6 +752,7 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   }
 
   if ((err = mark(p, MOE_STAGE_COMBINE, s)) != hipSuccess) return err;
+  if (side && (err = hipStreamWaitEvent(s, p.shared_done, 0)) != hipSuccess) return err;
   {
     const int64_t sb = p.has_shared ? routed_rows : (int64_t)-1;
     const dim3 grid((unsigned)p.T), blk(256);

@@ -89,6 +89,11 @@ struct ExpertPlan {
   int max_tiles, tile_rows, n_shared_tiles;
   void *h, *yrows, *y;
   hipEvent_t *events;    // null, or [MOE_STAGE_COUNT + 1] stage timing events
+  // Non-null when launch_shared_expert has put the shared expert (and, for
+  // MXFP8, x's quantised copy) on a side stream: launch_experts then leaves
+  // them out, waits for xq_ready before the routed up GEMM and for
+  // shared_done before the combine.
+  hipEvent_t shared_done, xq_ready;
 };
 
 // Rows per GEMM tile chosen for a layer of T tokens (depends on the
@@ -96,6 +101,12 @@ struct ExpertPlan {
 int choose_tile_rows(const moe_config &cfg, int64_t T);
 
 hipError_t launch_experts(const ExpertPlan &p, hipStream_t s);
+
+// The shared expert of a bf16-activation FP4 / FP8 expert layer on stream s: H rows
+// [T k, T k + T) = SwiGLU_shared(x), Y rows [T k, T k + T) = H W_down^T (both
+// only need x), after x's MXFP8 copy for MXFP8 layers (xq_ready recorded
+// after it).  Needs nothing the routing or the permutation writes.
+hipError_t launch_shared_expert(const ExpertPlan &p, hipStream_t s, hipEvent_t xq_ready);
 
 // FP4 -> FP8 E4M3 in 128 x 128 blocks (moe_redequant_fp8).
 hipError_t launch_redequant_fp8(const uint8_t *codes, const uint8_t *scales, int64_t n_mat, int N,

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -131,6 +132,38 @@ int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Side stream of a device for work that needs x alone (the shared expert, the
+// MXFP8 copy of x), with the events that fork it from and join it to the
+// caller's stream.  Created on a device's first forward call (default
+// priority, non-blocking) and kept until the process ends.  Forward calls
+// enqueue under side_mutex, so calls from several host threads on one device
+// never interleave their fork/join records on these events.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, xq_ready = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream side_streams[kMaxDevices];
+std::mutex side_mutex;
+
+// Call with side_mutex held.
+hipError_t side_stream(SideStream **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream &ss = side_streams[dev];
+  if (!ss.stream) {
+    SideStream n;
+    if ((e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    for (hipEvent_t *ev : {&n.fork, &n.join, &n.xq_ready})
+      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+    ss = n;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
 
 // The k smallest primes above m (trial division; m < 2^31, k <= 16).
 void primes_above(int64_t m, int k, int64_t *out) {
@@ -358,36 +391,8 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   const int k = cfg->n_activated_experts;
   const bool hash = cfg->route_mode != MOE_ROUTE_LEARNED;
 
-  hipError_t e;
-  if (events && hipEventRecord(events[MOE_STAGE_ROUTE], s) != hipSuccess) return MOE_ERR_HIP;
-  if (hash) {
-    if ((e = moe::launch_clear_flags(flags, s)) != hipSuccess) return MOE_ERR_HIP;
-    if (cfg->route_mode == MOE_ROUTE_NGRAM_HASH) {
-      int64_t q[16];
-      primes_above(cfg->vocab_size, k, q);
-      e = moe::launch_route_ngram(*cfg, token_ids, q, T, route_w, route_idx, flags, s);
-    } else {
-      e = moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, route_w, route_idx, flags, s);
-    }
-  } else {
-    e = moe::launch_route_learned(*cfg, x, w->gate_w, w->gate_bias, T, route_w, route_idx, s,
-                                  moe::route_logits_floats(*cfg, T) ? logits : nullptr);
-  }
-  if (e != hipSuccess) return MOE_ERR_HIP;
-
-  moe::TileSpec ts;
-  ts.tiles = tiles;
-  ts.tile_count = tile_count;
-  ts.tile_rows = L.tile_rows;
-  ts.n_shared_tiles = cfg->n_shared_experts ? (int)((T + L.tile_rows - 1) / L.tile_rows) : 0;
-  ts.shared_rows_tok = sorted_tok + T * k;
-  ts.route_w = route_w;
-  ts.sorted_w = sorted_w;
-  if (events && hipEventRecord(events[MOE_STAGE_PERMUTE], s) != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_permute(cfg->n_routed_experts, k, T, route_idx, counts, offsets, sorted_tok,
-                          sorted_slot, inverse, flags, &ts, /*clear_flags=*/!hash, s, perm_hist);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-
+  const int n_shared_tiles =
+      cfg->n_shared_experts ? (int)((T + L.tile_rows - 1) / L.tile_rows) : 0;
   moe::ExpertPlan p;
   p.T = T;
   p.k = k;
@@ -417,11 +422,67 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   p.tile_count = tile_count;
   p.max_tiles = L.max_tiles;
   p.tile_rows = L.tile_rows;
-  p.n_shared_tiles = ts.n_shared_tiles;
+  p.n_shared_tiles = n_shared_tiles;
   p.h = base + L.h;
   p.yrows = base + L.yrows;
   p.y = y;
   p.events = events;
+  p.shared_done = nullptr;
+  p.xq_ready = nullptr;
+
+  // FP4 / FP8 expert layers: the shared expert (bf16, launches of its own) and
+  // the MXFP8 copy of x need x alone, so they run on the side stream, forked
+  // here, while the routing and the permutation (latency-bound, most CUs
+  // idle) run on s; s waits for x's copy before the routed up GEMM and joins
+  // the side stream before the combine.  bf16 expert layers keep the shared
+  // tiles inside the grouped launches, where they share the CUs with the
+  // HBM-bound routed tiles (on the side stream its dense GEMM held every CU
+  // and delayed the routing: 2 % slower at the V3 prefill shape).
+  std::unique_lock<std::mutex> lock(side_mutex);
+  hipError_t e;
+  const bool low_precision = cfg->expert_dtype == MOE_DTYPE_FP4_E2M1 ||
+                             cfg->expert_dtype == MOE_DTYPE_FP8_E4M3_B128;
+  if (cfg->act_dtype == MOE_DTYPE_BF16 && low_precision && (p.has_shared || p.mx)) {
+    SideStream *ss = nullptr;
+    if ((e = side_stream(&ss)) != hipSuccess) return MOE_ERR_HIP;
+    if (hipEventRecord(ss->fork, s) != hipSuccess ||
+        hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (moe::launch_shared_expert(p, ss->stream, ss->xq_ready) != hipSuccess ||
+        hipEventRecord(ss->join, ss->stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    p.shared_done = ss->join;
+    p.xq_ready = p.mx ? ss->xq_ready : nullptr;
+  }
+
+  if (events && hipEventRecord(events[MOE_STAGE_ROUTE], s) != hipSuccess) return MOE_ERR_HIP;
+  if (hash) {
+    if ((e = moe::launch_clear_flags(flags, s)) != hipSuccess) return MOE_ERR_HIP;
+    if (cfg->route_mode == MOE_ROUTE_NGRAM_HASH) {
+      int64_t q[16];
+      primes_above(cfg->vocab_size, k, q);
+      e = moe::launch_route_ngram(*cfg, token_ids, q, T, route_w, route_idx, flags, s);
+    } else {
+      e = moe::launch_route_hash(*cfg, token_ids, w->tid2eid, T, route_w, route_idx, flags, s);
+    }
+  } else {
+    e = moe::launch_route_learned(*cfg, x, w->gate_w, w->gate_bias, T, route_w, route_idx, s,
+                                  moe::route_logits_floats(*cfg, T) ? logits : nullptr);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  moe::TileSpec ts;
+  ts.tiles = tiles;
+  ts.tile_count = tile_count;
+  ts.tile_rows = L.tile_rows;
+  ts.n_shared_tiles = n_shared_tiles;
+  ts.shared_rows_tok = sorted_tok + T * k;
+  ts.route_w = route_w;
+  ts.sorted_w = sorted_w;
+  if (events && hipEventRecord(events[MOE_STAGE_PERMUTE], s) != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_permute(cfg->n_routed_experts, k, T, route_idx, counts, offsets, sorted_tok,
+                          sorted_slot, inverse, flags, &ts, /*clear_flags=*/!hash, s, perm_hist);
+  if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_experts(p, s));
 }
 
