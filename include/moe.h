@@ -345,6 +345,14 @@ int moe_permute(const moe_config *cfg, const int32_t *indices, int64_t T,
  *   ws  device workspace of at least moe_workspace_size(cfg, T) bytes,
  *       256-byte aligned; its sub-buffers (moe_ws_layout) hold the
  *       routing, permutation and intermediates of this call afterwards.
+ *   stream  must belong to the current device.
+ * FP4 / FP8 expert layers (bf16 activations) run the shared expert and the
+ * MXFP8 copy of x on a side stream of the library, forked from `stream` at
+ * the start of the call and joined into it before the combine, so they
+ * overlap the routing; all work of the call is complete when `stream`
+ * reaches the call's end.  The side stream and three events are created on a
+ * device's first such call (default priority; kept until the process ends),
+ * and calls from several host threads enqueue one at a time.
  * T == 0 is a no-op.  MOE_ERR_WORKSPACE if ws is NULL, misaligned or small. */
 int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                 const int32_t *token_ids, int64_t T, void *y,
@@ -353,7 +361,8 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
 /* Stages of moe_forward in launch order (for moe_forward_profiled). */
 #define MOE_STAGE_ROUTE 0     /* router kernel (or hash gather)                  */
 #define MOE_STAGE_PERMUTE 1   /* permute kernel                                 */
-#define MOE_STAGE_GEMM1 2     /* gate|up grouped GEMM + SwiGLU (routed + shared) */
+#define MOE_STAGE_GEMM1 2     /* gate|up grouped GEMM + SwiGLU (routed, and the
+                                 shared expert of bf16 expert layers)            */
 #define MOE_STAGE_GEMM2 3     /* down grouped GEMM x gate value                  */
 #define MOE_STAGE_COMBINE 4   /* gather-combine into y                          */
 #define MOE_STAGE_COUNT 5
@@ -363,7 +372,8 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
  *   events (host) [MOE_STAGE_COUNT + 1] hipEvent_t handles created by the
  *   caller (hipEventCreate); event i precedes stage i, event COUNT follows
  *   the combine.  Results are identical to moe_forward's.  A failed
- *   hipEventRecord returns MOE_ERR_HIP. */
+ *   hipEventRecord returns MOE_ERR_HIP.  Work on the side stream (the shared
+ *   expert of FP4 / FP8 layers) overlaps the stages and belongs to none. */
 int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void *x,
                          const int32_t *token_ids, int64_t T, void *y,
                          void *ws, size_t ws_bytes, void **events, void *stream);
