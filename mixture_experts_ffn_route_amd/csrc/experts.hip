@@ -402,14 +402,16 @@ __global__ __launch_bounds__(256) void expert_down_f32(
 
 // ---------------------------------------------------------------------------
 // Combine: y[t] = sum_j Y[inverse[t, j]] + Y[T*k + t], fp32 sum in slot order.
-// One workgroup per token.  The token's k permuted rows (and its shared row)
-// are looked up first; then every lane issues all k+1 16-byte loads of its
-// 8 columns before adding them in slot order, shared row last (a dropped pair,
-// inverse = -1, contributes nothing).
+// One workgroup per token with one lane per 8-column chunk (dim/8 lanes
+// rounded up to whole waves, at most 1024; wider rows loop).  The token's k
+// permuted rows (and its shared row) are looked up first; then every lane
+// issues all k+1 16-byte loads of its chunk before adding them in slot order,
+// shared row last (a dropped pair, inverse = -1, contributes nothing).
 template <int KMAX>
-__global__ __launch_bounds__(256) void combine_bf16(const bf16 *Y, const int32_t *inverse,
-                                                    int k, int dim, int64_t shared_base,
-                                                    bf16 *y) {
+__global__ __launch_bounds__(1024) void combine_bf16(const bf16 *__restrict__ Y,
+                                                     const int32_t *__restrict__ inverse,
+                                                     int k, int dim, int64_t shared_base,
+                                                     bf16 *__restrict__ y) {
   const int64_t t = blockIdx.x;
   int64_t row[KMAX + 1];
   bool use[KMAX + 1];
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16 *Y, const int32_t
   }
   use[KMAX] = shared_base >= 0;
   row[KMAX] = shared_base >= 0 ? shared_base + t : 0;
-  for (int c = threadIdx.x * 8; c < dim; c += 256 * 8) {
+  for (int c = threadIdx.x * 8; c < dim; c += blockDim.x * 8) {
     bf16x8 v[KMAX + 1];
 #pragma unroll
     for (int j = 0; j <= KMAX; ++j) v[j] = *(const bf16x8 *)(Y + row[j] * dim + c);
@@ -755,7 +757,8 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
   if (side && (err = hipStreamWaitEvent(s, p.shared_done, 0)) != hipSuccess) return err;
   {
     const int64_t sb = p.has_shared ? routed_rows : (int64_t)-1;
-    const dim3 grid((unsigned)p.T), blk(256);
+    const int lanes = (p.dim / 8 + 63) / 64 * 64;
+    const dim3 grid((unsigned)p.T), blk((unsigned)(lanes < 1024 ? lanes : 1024));
     const bf16 *Y = (const bf16 *)p.yrows;
     bf16 *yo = (bf16 *)p.y;
     if (p.k <= 2)
