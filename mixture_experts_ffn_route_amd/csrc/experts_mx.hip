@@ -303,11 +303,14 @@ constexpr int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
 struct MxRing {
   uint8_t *a[4];
   uint8_t *b[8];
-  uint8_t *bs;    // FP8 weights: the slab's block scales, [matrix][stage]
+  uint8_t *bs;    // FP8 weights: the slab's block scales, [matrix][block][stage]
 };
 
 // Most 128-input stages the FP8-weight form keeps block scales for (K <= 32768).
 constexpr int kMxF8MaxStages = 256;
+
+// 128-column FP8 weight blocks in a slab of SC 16-column blocks.
+constexpr int mx_f8_blocks(int sc) { return sc > 8 ? sc / 8 : 1; }
 
 // Row-split tile for tiles of 4 and more row blocks.  Each wave owns MW =
 // MBE/WAVES row blocks and every column of the slab: SC 16-column blocks of
@@ -326,8 +329,9 @@ constexpr int kMxF8MaxStages = 256;
 // FP8 weights (F8, re-dequantised from FP4 by moe_redequant_fp8): a fragment
 // is 2 KB stored in operand order -- lane (c, q) reads 16 bytes at
 // (q*16 + c)*16 and 16 at 1024 + (q*16 + c)*16 -- and is copied as two 1 KB
-// units; its scale is the one E8M0 byte of the 128 x 128 block, the same for
-// the whole slab and stage, kept in LDS for all stages of the tile.
+// units; its scale is the E8M0 byte of its 128 x 128 block: a slab covers
+// SC / 8 such blocks of each matrix (at least one: narrower slabs lie inside
+// one), and their bytes for every stage of the tile are kept in LDS.
 //
 // LDS form of an FP4 weight fragment.  Tiled weights: the 16-byte chunk (t, g, p)
 // of the stage (64-input tile t, 8-byte group g, column pair p) is stored at
@@ -457,12 +461,14 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
 
   const int nst = K / BK;
   const int last = nst - 1;
+  constexpr int BPS = mx_f8_blocks(SC);           // FP8 weight blocks per slab and matrix
+  static_assert(!F8 || SC % 8 == 0 || SC < 8, "a slab covers whole 128-column blocks");
   if constexpr (F8) {
-    // block scales of this slab (one 128-row block of each matrix) for every stage
-    const int br = col0 >> 7;
-    for (int i = threadIdx.x; i < NB * nst; i += WAVES * 64) {
-      const int b = i / nst, st = i - b * nst;
-      ring.bs[i] = g.S[b][((int64_t)t.grp * (N / 128) + br) * nst + st];
+    // block scales of this slab (BPS 128-row blocks of each matrix) for every stage
+    const int br0 = col0 >> 7;
+    for (int i = threadIdx.x; i < NB * BPS * nst; i += WAVES * 64) {
+      const int bj = i / nst, st = i - bj * nst, b = bj / BPS, j = bj - b * BPS;
+      ring.bs[i] = g.S[b][((int64_t)t.grp * (N / 128) + br0 + j) * nst + st];
     }
     __syncthreads();
   }
@@ -518,10 +524,10 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
     // weight fragments are read one ahead of their MFMAs
     i32x8 bv[2];
     int sbv[2];
-    int sblk[NB];
+    int sblk[NB * BPS];
     if constexpr (F8) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) sblk[b] = ring.bs[b * nst + st];
+      for (int bj = 0; bj < NB * BPS; ++bj) sblk[bj] = ring.bs[bj * nst + st];
     }
     auto read_frag = [&](int f, int buf) {
       if constexpr (F8) {
@@ -529,7 +535,7 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
         const u32x4 hi = *(const u32x4 *)(bslot + f * FRAG + boff1);
         bv[buf] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sbv[buf] = sblk[f / SC];
+        sbv[buf] = sblk[(f / SC) * BPS + (f % SC) / (SC / BPS)];
       } else {
         const uint2 lo = *(const uint2 *)(bslot + f * FRAG + boff0);
         const uint2 hi = *(const uint2 *)(bslot + f * FRAG + boff1);
@@ -650,7 +656,7 @@ void grouped_gemm_mx_rs(const GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t B5[NSB > 5 ? SB : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t B6[NSB > 6 ? SB : 1];
   __shared__ __attribute__((aligned(1024))) uint8_t B7[NSB > 7 ? SB : 1];
-  __shared__ uint8_t BS[F8 ? NB * kMxF8MaxStages : 1];
+  __shared__ uint8_t BS[F8 ? NB * mx_f8_blocks(SC) * kMxF8MaxStages : 1];
   const MxRing ring{{A0, A1, A2, A3}, {B0, B1, B2, B3, B4, B5, B6, B7}, BS};
   int tile, slab;
   if (!gemm_work_item(g, &tile, &slab)) return;
@@ -717,10 +723,17 @@ hipError_t run_gemm_mx(GemmArgs a, int max_tiles, hipStream_t s) {
 template <int NB, int MB>
 hipError_t run_gemm_mx_mb(GemmArgs a, int max_tiles, hipStream_t s) {
   if (a.b_fp8) {
-    // FP8 weights (2 KB fragments): 64 gate|up or 128 down columns per slab;
-    // decode tiles run as 4-block tiles
+    // FP8 weights (2 KB fragments): tiles of up to 12 row blocks take 128 gate|up
+    // or 256 down columns per slab with a 2-stage activation ring and a
+    // 3-stage weight ring (146 KB of LDS); taller tiles, or widths that do
+    // not divide, half that with 3 + 3 stages.  Decode tiles run as 4-block
+    // tiles.
     constexpr int SC8 = NB == 2 ? 4 : 8;
     if (a.N % (SC8 * 16) != 0 || a.K / 128 > kMxF8MaxStages) return hipErrorInvalidValue;
+    if constexpr (MB <= 12) {
+      if (a.N % (2 * SC8 * 16) == 0)
+        return run_gemm_mx_rs<4, NB, 2 * SC8, (MB < 4 ? 4 : MB), 2, 3, 1, true>(a, max_tiles, s);
+    }
     return run_gemm_mx_rs<4, NB, SC8, (MB < 4 ? 4 : MB), 3, 3, 1, true>(a, max_tiles, s);
   }
   if constexpr (MB >= 4) {
