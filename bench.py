@@ -3,11 +3,11 @@
 
 A step is one full forward of the layer (route -> permute -> grouped GEMM1
 with SwiGLU -> grouped GEMM2 -> combine with the shared expert) over one
-batch of synthetic tokens, through the C ABI (moe_forward_profiled).  Inputs
-and weights are resident in HBM before the timed region starts.  For FP4 /
-FP8 expert layers the library runs the shared expert on a side stream during
-routing; the step time covers it (the combine waits for it), the stage times
-do not.
+batch of synthetic tokens, through the C ABI (moe_forward_ex with stage
+events and a second stream).  Inputs and weights are resident in HBM before
+the timed region starts.  For FP4 / FP8 expert layers the library runs the
+shared expert on the second stream during routing; the step time covers it
+(the combine waits for it), the stage times do not.
 
 Prints one JSON line:
   value        tokens/s of the DeepSeek-V3-shaped prefill layer (T=4096)
@@ -83,7 +83,7 @@ def algorithmic_counts(wl, counts):
     sh = cfg.n_shared_experts
     rows = T * k + T * sh
     # the up-GEMM stage: FP4 / FP8 expert layers run the shared expert on the
-    # library's side stream, concurrently with the routing, outside the stage
+    # second stream (moe_forward_ex), concurrently with the routing, outside the stage
     sh1 = 0 if (cfg.act_dtype == "bf16" and (cfg.expert_dtype == "fp4" or wl.fp8_weights)) else sh
     gemm1 = {"flops": 4.0 * d * I * (T * k + T * sh1),
              "bytes": n_hit * 2 * mat + sh1 * 2 * I * d * eb + T * d * eb}
@@ -179,6 +179,20 @@ def run_weights(wl, layer, B, layout):
     return B.pack_layer(wl.cfg, layer)
 
 
+_SIDE_STREAM = None
+
+
+def side_stream(torch):
+    """The second stream moe_forward_ex gets, created once per process before
+    any other (HIP spreads streams over a few hardware queues, four by
+    default; a side stream that shares the main stream's queue runs in its
+    order, not beside it, and every new stream is another draw)."""
+    global _SIDE_STREAM
+    if _SIDE_STREAM is None:
+        _SIDE_STREAM = torch.cuda.Stream()
+    return _SIDE_STREAM
+
+
 def time_workload(wl, layer, steps, warmup, B, torch, cfg=None):
     cfg, T = (cfg or wl.cfg), wl.T
     dev = layer["x"].device
@@ -186,15 +200,16 @@ def time_workload(wl, layer, steps, warmup, B, torch, cfg=None):
     y = torch.empty_like(layer["x"])
     nst = len(B.MOE_STAGES)
     ev = B.HipEvents((nst + 1) * steps)
+    side = side_stream(torch)           # second stream for the work that needs x alone
     for _ in range(warmup):
-        B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y, ws)
+        B.moe_forward_ex(cfg, layer, layer["x"], layer["token_ids"], T, y, ws, side_stream=side)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for s in range(steps):
-        B.moe_forward_profiled(cfg, layer, layer["x"], layer["token_ids"], T, y, ws,
-                               ev.handles[s * (nst + 1):(s + 1) * (nst + 1)])
+        B.moe_forward_ex(cfg, layer, layer["x"], layer["token_ids"], T, y, ws,
+                         events=ev.handles[s * (nst + 1):(s + 1) * (nst + 1)], side_stream=side)
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
@@ -337,6 +352,7 @@ def main():
     from mixture_experts_ffn_route_amd import synth
 
     dev = torch.device("cuda:0")
+    side_stream(torch)                  # before any other stream (see side_stream)
     wl = C.FULL_WORKLOADS[args.workload]
     log(f"generating {wl.name} inputs on {torch.cuda.get_device_name(0)}")
     t = time.time()
@@ -385,7 +401,8 @@ def main():
     names = ([args.decode] if args.decode else []) + [n for n in args.extra.split(",") if n]
     for name in names:
         w2 = C.FULL_WORKLOADS[name]
-        if w2.cfg == wl.cfg and w2.seed == wl.seed and max(w2.T, w2.x_rows) == wl.T:
+        if (w2.cfg == wl.cfg and w2.seed == wl.seed and w2.fp8_weights == wl.fp8_weights
+                and max(w2.T, w2.x_rows) == wl.T):
             # same layer and weights; x is the first T rows of the same draw
             l2 = dict(rlayer)
             l2["x"] = layer["x"][:w2.T].contiguous()

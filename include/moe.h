@@ -345,14 +345,7 @@ int moe_permute(const moe_config *cfg, const int32_t *indices, int64_t T,
  *   ws  device workspace of at least moe_workspace_size(cfg, T) bytes,
  *       256-byte aligned; its sub-buffers (moe_ws_layout) hold the
  *       routing, permutation and intermediates of this call afterwards.
- *   stream  must belong to the current device.
- * FP4 / FP8 expert layers (bf16 activations) run the shared expert and the
- * MXFP8 copy of x on a side stream of the library, forked from `stream` at
- * the start of the call and joined into it before the combine, so they
- * overlap the routing; all work of the call is complete when `stream`
- * reaches the call's end.  The side stream and three events are created on a
- * device's first such call (default priority; kept until the process ends),
- * and calls from several host threads enqueue one at a time.
+ * Everything is enqueued on `stream`; nothing persists between calls.
  * T == 0 is a no-op.  MOE_ERR_WORKSPACE if ws is NULL, misaligned or small. */
 int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                 const int32_t *token_ids, int64_t T, void *y,
@@ -361,8 +354,8 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
 /* Stages of moe_forward in launch order (for moe_forward_profiled). */
 #define MOE_STAGE_ROUTE 0     /* router kernel (or hash gather)                  */
 #define MOE_STAGE_PERMUTE 1   /* permute kernel                                 */
-#define MOE_STAGE_GEMM1 2     /* gate|up grouped GEMM + SwiGLU (routed, and the
-                                 shared expert of bf16 expert layers)            */
+#define MOE_STAGE_GEMM1 2     /* gate|up grouped GEMM + SwiGLU (routed + shared;
+                                 routed only with a side stream, moe_forward_ex) */
 #define MOE_STAGE_GEMM2 3     /* down grouped GEMM x gate value                  */
 #define MOE_STAGE_COMBINE 4   /* gather-combine into y                          */
 #define MOE_STAGE_COUNT 5
@@ -372,11 +365,33 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
  *   events (host) [MOE_STAGE_COUNT + 1] hipEvent_t handles created by the
  *   caller (hipEventCreate); event i precedes stage i, event COUNT follows
  *   the combine.  Results are identical to moe_forward's.  A failed
- *   hipEventRecord returns MOE_ERR_HIP.  Work on the side stream (the shared
- *   expert of FP4 / FP8 layers) overlaps the stages and belongs to none. */
+ *   hipEventRecord returns MOE_ERR_HIP. */
 int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void *x,
                          const int32_t *token_ids, int64_t T, void *y,
                          void *ws, size_t ws_bytes, void **events, void *stream);
+
+/* moe_forward with optional stage events (as moe_forward_profiled; NULL: none)
+ * and an optional second stream of the caller, `side_stream` (NULL: none;
+ * not `stream` itself), on the same device.  For FP4 / FP8 expert layers with
+ * bf16 activations the work that needs x alone -- the MXFP8 copy of x and the
+ * shared expert -- is enqueued on side_stream, forked from `stream` at the
+ * start of the call, so it runs while the latency-bound routing and
+ * permutation run on `stream` (the shared expert's output is added to the
+ * routed sum and depends on x alone, "DeepSeek V4.1 - Add shared", formula
+ * of Delta_ffn; the shared experts' work placed in the routing's idle time,
+ * "From One Giant FFN to 384 Tiny Experts", Ch.5.1); `stream` waits for x's copy before
+ * the routed up GEMM and joins side_stream before the combine, so all work of
+ * the call is ordered before whatever the caller enqueues on `stream` next,
+ * and side_stream gets nothing the next call's fork does not order after
+ * this call.  The fork and join events (three per host thread and device)
+ * are created on a thread's first such call and kept until the process
+ * ends; nothing else persists.  The stage events then time the routed launches
+ * only.  Results are bit-identical to moe_forward's (the same kernels in the
+ * same order per output).  Other layers ignore side_stream. */
+int moe_forward_ex(const moe_config *cfg, const moe_weights *w, const void *x,
+                   const int32_t *token_ids, int64_t T, void *y,
+                   void *ws, size_t ws_bytes, void **events, void *stream,
+                   void *side_stream);
 
 /* Roofline probes: the achievable HBM read rate and bf16 MFMA rate of the
  * GPU, measured with the instruction forms the layer kernels use (16-byte

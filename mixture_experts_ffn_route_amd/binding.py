@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout",
     "moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_profiled",
     "moe_pack_weights", "moe_build_tid2eid_multistart", "moe_update_bias", "moe_probe_read",
-    "moe_probe_mfma", "moe_redequant_fp8",
+    "moe_probe_mfma", "moe_redequant_fp8", "moe_forward_ex",
 )
 MOE_STAGES = ("route", "permute", "gemm1", "gemm2", "combine")
 
@@ -87,8 +87,11 @@ def _load():
     lib.moe_redequant_fp8.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp]
     lib.moe_forward_profiled.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t,
                                          ctypes.POINTER(ctypes.c_void_p), vp]
+    lib.moe_forward_ex.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t,
+                                   ctypes.POINTER(ctypes.c_void_p), vp, vp]
     for f in ("moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout", "moe_route",
-              "moe_permute", "moe_forward", "moe_forward_profiled", "moe_pack_weights",
+              "moe_permute", "moe_forward", "moe_forward_profiled", "moe_forward_ex",
+              "moe_pack_weights",
               "moe_build_tid2eid_multistart", "moe_update_bias", "moe_probe_read",
               "moe_probe_mfma"):
         getattr(lib, f).restype = ctypes.c_int
@@ -296,6 +299,18 @@ def moe_forward_profiled(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, w
                                      _ptr(x), _ptr(token_ids), T, _ptr(y), _ptr(ws),
                                      ws.numel() * ws.element_size(), arr, _stream(stream)),
            "moe_forward_profiled")
+
+
+def moe_forward_ex(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, ws, events=None,
+                   stream=None, side_stream=None):
+    """events: None or len(MOE_STAGES) + 1 raw hipEvent_t handles; side_stream:
+    None, or a torch stream / raw handle other than `stream`."""
+    arr = (ctypes.c_void_p * len(events))(*events) if events is not None else None
+    side = None if side_stream is None else _stream(side_stream)
+    _check(_lib.moe_forward_ex(ctypes.byref(config_c(cfg)), ctypes.byref(weights_c(layer)),
+                               _ptr(x), _ptr(token_ids), T, _ptr(y), _ptr(ws),
+                               ws.numel() * ws.element_size(), arr, _stream(stream), side),
+           "moe_forward_ex")
 
 
 class HipEvents:

@@ -7,7 +7,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -133,35 +132,31 @@ int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Side stream of a device for work that needs x alone (the shared expert, the
-// MXFP8 copy of x), with the events that fork it from and join it to the
-// caller's stream.  Created on a device's first forward call (default
-// priority, non-blocking) and kept until the process ends.  Forward calls
-// enqueue under side_mutex, so calls from several host threads on one device
-// never interleave their fork/join records on these events.
-struct SideStream {
-  hipStream_t stream = nullptr;
+// Events that fork a caller's side stream from its main stream and join it
+// back: three per host thread and device, created on the thread's first call
+// with a side stream on that device and kept until the process ends.  A
+// thread enqueues its calls one after another, and a wait takes the record
+// made just before it, so the next call may record the same events again;
+// no other thread uses them.
+struct SideEvents {
   hipEvent_t fork = nullptr, join = nullptr, xq_ready = nullptr;
 };
 constexpr int kMaxDevices = 64;
-SideStream side_streams[kMaxDevices];
-std::mutex side_mutex;
 
-// Call with side_mutex held.
-hipError_t side_stream(SideStream **out) {
+hipError_t side_events(SideEvents **out) {
+  thread_local SideEvents per_device[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  SideStream &ss = side_streams[dev];
-  if (!ss.stream) {
-    SideStream n;
-    if ((e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking)) != hipSuccess) return e;
-    for (hipEvent_t *ev : {&n.fork, &n.join, &n.xq_ready})
-      if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
-    ss = n;
+  SideEvents &ev = per_device[dev];
+  if (!ev.xq_ready) {
+    SideEvents n;
+    for (hipEvent_t *p : {&n.fork, &n.join, &n.xq_ready})
+      if ((e = hipEventCreateWithFlags(p, hipEventDisableTiming)) != hipSuccess) return e;
+    ev = n;
   }
-  *out = &ss;
+  *out = &ev;
   return hipSuccess;
 }
 
@@ -351,7 +346,7 @@ int moe_permute(const moe_config *cfg, const int32_t *indices, int64_t T, int32_
 
 static int forward_impl(const moe_config *cfg, const moe_weights *w, const void *x,
                         const int32_t *token_ids, int64_t T, void *y, void *ws, size_t ws_bytes,
-                        hipEvent_t *events, void *stream) {
+                        hipEvent_t *events, void *stream, void *side_stream) {
   moe_ws_layout L;
   int st = make_layout(cfg, T, &L);
   if (st != MOE_OK) return st;
@@ -430,29 +425,31 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   p.shared_done = nullptr;
   p.xq_ready = nullptr;
 
-  // FP4 / FP8 expert layers: the shared expert (bf16, launches of its own) and
-  // the MXFP8 copy of x need x alone, so they run on the side stream, forked
-  // here, while the routing and the permutation (latency-bound, most CUs
-  // idle) run on s; s waits for x's copy before the routed up GEMM and joins
-  // the side stream before the combine.  bf16 expert layers keep the shared
-  // tiles inside the grouped launches, where they share the CUs with the
-  // HBM-bound routed tiles (on the side stream its dense GEMM held every CU
-  // and delayed the routing: 2 % slower at the V3 prefill shape).
-  std::unique_lock<std::mutex> lock(side_mutex);
+  // With a side stream, FP4 / FP8 expert layers put the shared expert (bf16,
+  // launches of its own) and the MXFP8 copy of x, which need x alone, on it:
+  // forked from s here, so they run while the routing and the permutation
+  // (latency-bound, most CUs idle) run on s; s waits for x's copy before the
+  // routed up GEMM and joins the side stream before the combine.  bf16 expert
+  // layers keep the shared tiles inside the grouped launches, where they
+  // share the CUs with the HBM-bound routed tiles (on a side stream the
+  // shared dense GEMM held every CU and delayed the routing: 2 % slower at
+  // the V3 prefill shape), and ignore the side stream.
   hipError_t e;
   const bool low_precision = cfg->expert_dtype == MOE_DTYPE_FP4_E2M1 ||
                              cfg->expert_dtype == MOE_DTYPE_FP8_E4M3_B128;
-  if (cfg->act_dtype == MOE_DTYPE_BF16 && low_precision && (p.has_shared || p.mx)) {
-    SideStream *ss = nullptr;
-    if ((e = side_stream(&ss)) != hipSuccess) return MOE_ERR_HIP;
-    if (hipEventRecord(ss->fork, s) != hipSuccess ||
-        hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+  if (side_stream && cfg->act_dtype == MOE_DTYPE_BF16 && low_precision &&
+      (p.has_shared || p.mx)) {
+    hipStream_t s2 = (hipStream_t)side_stream;
+    SideEvents *side = nullptr;
+    if (side_events(&side) != hipSuccess) return MOE_ERR_HIP;
+    if (hipEventRecord(side->fork, s) != hipSuccess ||
+        hipStreamWaitEvent(s2, side->fork, 0) != hipSuccess)
       return MOE_ERR_HIP;
-    if (moe::launch_shared_expert(p, ss->stream, ss->xq_ready) != hipSuccess ||
-        hipEventRecord(ss->join, ss->stream) != hipSuccess)
+    if (moe::launch_shared_expert(p, s2, side->xq_ready) != hipSuccess ||
+        hipEventRecord(side->join, s2) != hipSuccess)
       return MOE_ERR_HIP;
-    p.shared_done = ss->join;
-    p.xq_ready = p.mx ? ss->xq_ready : nullptr;
+    p.shared_done = side->join;
+    p.xq_ready = p.mx ? side->xq_ready : nullptr;
   }
 
   if (events && hipEventRecord(events[MOE_STAGE_ROUTE], s) != hipSuccess) return MOE_ERR_HIP;
@@ -534,7 +531,7 @@ int moe_redequant_fp8(const uint8_t *codes, const uint8_t *scales, int64_t n_mat
 int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                 const int32_t *token_ids, int64_t T, void *y, void *ws, size_t ws_bytes,
                 void *stream) {
-  return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, nullptr, stream);
+  return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, nullptr, stream, nullptr);
 }
 
 int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void *x,
@@ -543,7 +540,19 @@ int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void
   if (!events) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
     if (!events[i]) return MOE_ERR_INVALID_ARG;
-  return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, (hipEvent_t *)events, stream);
+  return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, (hipEvent_t *)events, stream,
+                      nullptr);
+}
+
+int moe_forward_ex(const moe_config *cfg, const moe_weights *w, const void *x,
+                   const int32_t *token_ids, int64_t T, void *y, void *ws, size_t ws_bytes,
+                   void **events, void *stream, void *side_stream) {
+  if (events)
+    for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
+      if (!events[i]) return MOE_ERR_INVALID_ARG;
+  if (side_stream && side_stream == stream) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, (hipEvent_t *)events, stream,
+                      side_stream);
 }
 
 int moe_probe_read(const void *buf, int64_t bytes, void *out, void *stream) {

@@ -279,3 +279,22 @@ def test_redequant_argument_checks():
     assert f(None, fake, 1, 128, 128, fake, fake, fake, None) == B.MOE_ERR_INVALID_ARG
     assert f(fake, fake, 1, 128, 128, fake, fake, None, None) == B.MOE_ERR_INVALID_ARG
     assert f(None, None, 0, 128, 128, None, None, None, None) == B.MOE_OK
+
+
+def test_forward_ex_argument_checks():
+    """Host-side checks of moe_forward_ex (no launch happens): the side
+    stream may not be the main stream, and a given event array must be full."""
+    cfg = C.V41_FLASH_FP4_MX.cfg
+    cfg_c = B.config_c(cfg)
+    w = B.MoeWeightsC()
+    fake = ctypes.c_void_p(0x100000)
+    f = B._lib.moe_forward_ex
+    s = ctypes.c_void_p(0x2000)
+    assert f(ctypes.byref(cfg_c), ctypes.byref(w), fake, None, 64, fake, fake, 1 << 30, None,
+             s, s) == B.MOE_ERR_INVALID_ARG
+    events = (ctypes.c_void_p * (len(B.MOE_STAGES) + 1))()
+    assert f(ctypes.byref(cfg_c), ctypes.byref(w), fake, None, 64, fake, fake, 1 << 30, events,
+             s, None) == B.MOE_ERR_INVALID_ARG
+    # T == 0 is a no-op that returns before any stream is touched
+    assert f(ctypes.byref(cfg_c), ctypes.byref(w), fake, None, 0, fake, fake, 0, None,
+             s, ctypes.c_void_p(0x3000)) == B.MOE_OK

@@ -1,13 +1,14 @@
-"""Stream ordering of moe_forward.  FP4 / FP8 expert layers run the shared
-expert and the MXFP8 copy of x on a library side stream forked from the
-caller's stream and joined before the combine; these tests check that the
-fork and join order the work correctly.  Every result must equal a lone
-call on the default stream bit for bit, because the layer is deterministic.
-The cases are: a call on a non-default stream, back-to-back calls that reuse
-one workspace with different inputs, and two host threads calling at once on
-streams of their own.  The accuracy bar against the oracle is the parity
-tests' job; bf16 expert layers, which use no side stream, are included as a
-control."""
+"""Stream ordering of moe_forward_ex with a second stream.  FP4 / FP8 expert
+layers then run the shared expert and the MXFP8 copy of x on the caller's
+side stream, forked from the main stream and joined before the combine;
+these tests check that the fork and join order the work correctly.  Every
+result must equal moe_forward's on the default stream bit for bit, because
+the layer is deterministic and both paths run the same kernels in the same
+order per output.  The cases are: a call on non-default streams, back-to-back
+calls that reuse one workspace with different inputs, and two host threads
+calling at once on streams of their own.  The accuracy bar against the oracle
+is the parity tests' job; bf16 expert layers, which ignore the side stream,
+are included as a control."""
 
 import threading
 
@@ -33,29 +34,30 @@ def _setup(name, dev):
     return wl, cfg, layer, x2
 
 
-def _forward(cfg, layer, x, T, ws, stream=None):
-    y = torch.empty_like(x)
-    B.moe_forward(cfg, layer, x, layer["token_ids"], T, y, ws, stream=stream)
-    return y
-
-
 def _lone(cfg, layer, x, T, dev):
+    """moe_forward (one stream) on the default stream."""
     ws = B.alloc_workspace(cfg, T, dev)
-    y = _forward(cfg, layer, x, T, ws)
+    y = torch.empty_like(x)
+    B.moe_forward(cfg, layer, x, layer["token_ids"], T, y, ws)
     torch.cuda.synchronize()
     return y
 
 
+def _forward_ex(cfg, layer, x, T, ws, y, stream, side):
+    B.moe_forward_ex(cfg, layer, x, layer["token_ids"], T, y, ws, stream=stream,
+                     side_stream=side)
+
+
 @pytest.mark.parametrize("name", NAMES)
-def test_non_default_stream(name, gpu):
+def test_side_stream_matches_one_stream(name, gpu):
     wl, cfg, layer, _ = _setup(name, gpu)
     ref = _lone(cfg, layer, layer["x"], wl.T, gpu)
     ws = B.alloc_workspace(cfg, wl.T, gpu)
     y = torch.empty_like(layer["x"])
     torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    print(f"[streams] {name}: forward on a non-default stream", flush=True)
-    B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], wl.T, y, ws, stream=s)
+    s, side = torch.cuda.Stream(), torch.cuda.Stream()
+    print(f"[streams] {name}: moe_forward_ex on two non-default streams", flush=True)
+    _forward_ex(cfg, layer, layer["x"], wl.T, ws, y, s, side)
     s.synchronize()
     assert torch.equal(y, ref)
 
@@ -67,8 +69,12 @@ def test_back_to_back_calls_reuse_one_workspace(name, gpu):
     ref2 = _lone(cfg, layer, x2, wl.T, gpu)
     assert not torch.equal(ref1, ref2)
     ws = B.alloc_workspace(cfg, wl.T, gpu)
+    ys = [torch.empty_like(layer["x"]) for _ in range(4)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
     print(f"[streams] {name}: 4 back-to-back calls on one workspace", flush=True)
-    ys = [_forward(cfg, layer, x, wl.T, ws) for x in (layer["x"], x2, layer["x"], x2)]
+    for x, y in zip((layer["x"], x2, layer["x"], x2), ys):
+        _forward_ex(cfg, layer, x, wl.T, ws, y, torch.cuda.current_stream(), side)
     torch.cuda.synchronize()
     for y, ref in zip(ys, (ref1, ref2, ref1, ref2)):
         assert torch.equal(y, ref)
@@ -79,7 +85,7 @@ def test_two_host_threads(name, gpu):
     wl, cfg, layer, x2 = _setup(name, gpu)
     refs = [_lone(cfg, layer, layer["x"], wl.T, gpu), _lone(cfg, layer, x2, wl.T, gpu)]
     inputs = [layer["x"], x2]
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    streams = [(torch.cuda.Stream(), torch.cuda.Stream()) for _ in range(2)]
     wss = [B.alloc_workspace(cfg, wl.T, gpu) for _ in range(2)]
     outs = [[torch.empty_like(layer["x"]) for _ in range(6)] for _ in range(2)]
     torch.cuda.synchronize()
@@ -89,9 +95,8 @@ def test_two_host_threads(name, gpu):
         try:
             torch.cuda.set_device(gpu)
             for j, y in enumerate(outs[i]):
-                B.moe_forward(cfg, layer, inputs[(i + j) % 2], layer["token_ids"], wl.T, y,
-                              wss[i], stream=streams[i])
-            streams[i].synchronize()
+                _forward_ex(cfg, layer, inputs[(i + j) % 2], wl.T, wss[i], y, *streams[i])
+            streams[i][0].synchronize()
         except Exception as e:                # reported by the main thread
             errors.append(e)
 
