@@ -111,3 +111,26 @@ def test_two_host_threads(name, gpu):
     for i in range(2):
         for j, y in enumerate(outs[i]):
             assert torch.equal(y, refs[(i + j) % 2]), (i, j)
+
+
+@pytest.mark.parametrize("name", ["fp4_mx_small", "v3_small"])
+def test_stage_events_with_side_stream(name, gpu):
+    """moe_forward_ex with stage events and a side stream: the same output, and
+    every stage interval recorded (non-negative, summing to at most the call)."""
+    wl, cfg, layer, _ = _setup(name, gpu)
+    ref = _lone(cfg, layer, layer["x"], wl.T, gpu)
+    ws = B.alloc_workspace(cfg, wl.T, gpu)
+    y = torch.empty_like(layer["x"])
+    nst = len(B.MOE_STAGES)
+    ev = B.HipEvents(nst + 1)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print(f"[streams] {name}: moe_forward_ex with stage events", flush=True)
+    B.moe_forward_ex(cfg, layer, layer["x"], layer["token_ids"], wl.T, y, ws, events=ev.handles,
+                     side_stream=side)
+    torch.cuda.synchronize()
+    stages = [ev.elapsed_ms(i, i + 1) for i in range(nst)]
+    total = ev.elapsed_ms(0, nst)
+    ev.close()
+    assert torch.equal(y, ref)
+    assert all(s >= 0.0 for s in stages) and sum(stages) <= total * 1.001 + 1e-3
