@@ -16,6 +16,8 @@ Prints one JSON line:
                bound, timed with HIP events on the library's stream
   cpu_baseline the float64 CPU oracle on a bounded sample of the same batch
   decode       the T=64 decode layer of the same weights (tokens/s, GB/s)
+  aux_ops      the path's other calls: selection-bias step, FP4 -> FP8
+               re-dequantisation, host tid2eid builders (beside the oracle's)
 """
 
 import argparse
@@ -243,6 +245,74 @@ def workload_report(wl, ms, stage_ms, counts, peak):
     }
 
 
+def aux_ops(torch, B, dev, synth, C):
+    """The path's other calls, each on the shape it serves: the selection-bias
+    step (V3: E=256), the load-time FP4 -> FP8 re-dequantisation (the
+    V4.1-Flash gate|up matrices, 384 x 1536 x 5120), and the host tid2eid
+    builders (m=32768 Zipf(1.1), n=64, k=4; greedy and an 8-order multi-start),
+    the last two beside the oracle's own time."""
+    import numpy as np
+    import oracle
+    out = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    cfg = C.V3_PREFILL.cfg
+    E, k, T = cfg.n_routed_experts, cfg.n_activated_experts, C.V3_PREFILL.T
+    g = torch.Generator(device="cpu").manual_seed(7)
+    counts = torch.randint(64, 200, (E,), generator=g, dtype=torch.int32).to(dev)
+    bias = torch.zeros(E, dtype=torch.float32, device=dev)
+    stats = torch.zeros(4, dtype=torch.float64, device=dev)
+    for _ in range(10):
+        B.moe_update_bias(cfg, counts, T, 1e-3, bias, stats)
+    torch.cuda.synchronize()
+    n = 200
+    e0.record()
+    for _ in range(n):
+        B.moe_update_bias(cfg, counts, T, 1e-3, bias, stats)
+    e1.record()
+    torch.cuda.synchronize()
+    out["update_bias"] = {"E": E, "us_per_call": round(e0.elapsed_time(e1) / n * 1e3, 2),
+                          "bound": "latency (one small workgroup)"}
+
+    n_mat, N, K = 384, 1536, 5120
+    codes = torch.randint(0, 256, (n_mat, N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.randint(118, 127, (n_mat, N, K // 32), dtype=torch.uint8, device=dev)
+    fp8 = torch.empty(n_mat * N * K, dtype=torch.uint8, device=dev)
+    bsc = torch.empty((n_mat, N // 128, K // 128), dtype=torch.uint8, device=dev)
+    lossy = torch.empty_like(bsc)
+    B.moe_redequant_fp8(codes, scales, n_mat, N, K, fp8, bsc, lossy)
+    torch.cuda.synchronize()
+    n = 5
+    e0.record()
+    for _ in range(n):
+        B.moe_redequant_fp8(codes, scales, n_mat, N, K, fp8, bsc, lossy)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = codes.numel() + scales.numel() + fp8.numel() + 2 * bsc.numel()
+    out["redequant_fp8"] = {"shape": [n_mat, N, K], "ms": round(ms, 4),
+                            **roofline_entry(0.0, nbytes, ms / 1e3, 1.0), "bytes": nbytes}
+    del codes, scales, fp8, bsc, lossy
+    torch.cuda.empty_cache()
+
+    p = synth.zipf_probs(32768, 1.1)
+    rng = np.random.default_rng(3)
+    orders = np.stack([rng.permutation(p.shape[0]) for _ in range(8)])
+    t = time.perf_counter()
+    B.moe_build_tid2eid(p, 64, 4)
+    lib_ms = (time.perf_counter() - t) * 1e3
+    t = time.perf_counter()
+    B.moe_build_tid2eid_multistart(p, 64, 4, orders)
+    lib_ms8 = (time.perf_counter() - t) * 1e3
+    t = time.perf_counter()
+    oracle.tid2eid_greedy(p, 64, 4)
+    ora_ms = (time.perf_counter() - t) * 1e3
+    out["tid2eid_host"] = {"m": int(p.shape[0]), "n": 64, "k": 4, "greedy_ms": round(lib_ms, 2),
+                           "multistart_8_ms": round(lib_ms8, 2),
+                           "oracle_greedy_ms": round(ora_ms, 2), "threads": 1}
+    return out
+
+
 def cpu_baseline(wl, layer, sample_tokens):
     """The float64 oracle, as it is, on the first `sample_tokens` tokens:
     routing + permutation + routed/shared SwiGLU forward."""
@@ -320,7 +390,9 @@ def main():
                     help="tokens of the batch the CPU oracle is timed on (about 10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
-                    help="skip measuring the achievable matmul / HBM-read denominators")
+                    help="skip measuring the achievable matmul / HBM-read denominators and "
+                         "timing the auxiliary calls (bias step, FP8 re-dequantisation, "
+                         "tid2eid builders)")
     ap.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
                     help="expert weight storage the timed steps read (tiled: packed once by "
                          "moe_pack_weights before timing)")
@@ -431,6 +503,10 @@ def main():
         denom = pk["hbm_read_gbs"] if r["unit"] == "GB/s" else pk["bf16_mfma_tflops"]
         r["frac_of_achievable"] = round(r["achieved"] / denom, 4)
         log(f"achievable: {pk}")
+    if not args.no_peaks:
+        log("timing the auxiliary calls")
+        out["aux_ops"] = aux_ops(torch, B, dev, synth, C)
+        log(f"aux: {out['aux_ops']}")
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_sample_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(wl, layer, args.cpu_sample_tokens)
