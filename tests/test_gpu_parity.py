@@ -215,3 +215,64 @@ def test_forward_hash_bad_token_id_flagged(gpu):
     v = B.workspace_views(cfg, T, ws)
     assert int(v["flags"][0]) & B.MOE_FLAG_TOKEN_ID_RANGE
     assert torch.all(v["route_weights"][5] == 0)
+
+
+def _mx_edge_rows(T, d, seed=11):
+    """bf16-exact rows whose 32-input blocks put the MXFP8 quantiser on its
+    edges: exact midpoints between neighbouring E4M3 codes (ties to even),
+    values between 448 and 512 after scaling (saturation), subnormal
+    midpoints, signed zeros, all-zero blocks and shared exponents at the
+    [-127, 127] clamp (amax 2^-126 and 2^100)."""
+    rng = np.random.default_rng(seed)
+    vals = oracle.E4M3_VALUES[:0x7F].copy()                  # finite non-negative codes
+    mids = (vals[:-1] + vals[1:]) / 2                        # includes subnormal midpoints
+    big = vals[vals >= 4.0]
+    sign = lambda n: rng.choice([-1.0, 1.0], size=n)
+    to_bf16 = lambda a: torch.from_numpy(a).to(torch.bfloat16).double().numpy()
+    x = np.zeros((T, d), dtype=np.float64)
+    for t in range(T):
+        for b in range(d // 32):
+            kind = (t * (d // 32) + b) % 5
+            if kind == 4:
+                continue                                     # all-zero block
+            blk = rng.choice(mids, size=32) * sign(32)
+            if kind == 1:
+                blk = rng.choice(vals, size=32) * sign(32)
+            if kind == 2:
+                blk[1:8] = to_bf16(rng.uniform(448, 512, size=7)) * sign(7)
+            if kind == 3:
+                blk[2:6] = [0.0, -0.0, 0.0, -0.0]
+            e = int(rng.integers(-20, 20))
+            if (t + b) % 17 == 0:
+                # amax 2^-120: the shared exponent -128 clamps to -127; every element
+                # stays an fp32 normal
+                e = -128
+                blk = rng.choice(big, size=32) * sign(32)
+            elif (t + b) % 17 == 1:
+                e = 92                                       # amax near 2^100
+            blk[0] = 256.0 + (rng.integers(0, 32) * 8)       # amax in [256, 512): X = e
+            x[t, 32 * b:32 * b + 32] = np.ldexp(blk, e)
+    return x
+
+
+@pytest.mark.parametrize("name", ["fp4_mx_small"])
+def test_mxfp8_codes_on_edge_values(name, gpu):
+    """The quantiser's codes and shared exponents on crafted ties, saturation,
+    subnormal and clamp cases, bit for bit against the oracle."""
+    wl = C.SMALL_WORKLOADS[name]
+    cfg, T = wl.cfg, wl.T
+    layer, _ = _layer(wl, gpu)
+    x64 = _mx_edge_rows(T, cfg.dim)
+    xb = torch.from_numpy(x64).to(torch.bfloat16)
+    assert np.array_equal(xb.double().numpy(), x64)            # exactly representable
+    layer["x"] = xb.to(gpu)
+    ws = B.alloc_workspace(cfg, T, gpu)
+    y = torch.empty_like(layer["x"])
+    print(f"[mx-edges] {name} T={T}", flush=True)
+    B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y, ws)
+    torch.cuda.synchronize()
+    v = B.workspace_views(cfg, T, ws)
+    codes, scales = oracle.mxfp8_quantize(x64)
+    np.testing.assert_array_equal(H.cpu_np(v["xq_scales"]), scales)
+    np.testing.assert_array_equal(H.cpu_np(v["xq"]), codes)
+    assert (scales == 0).any() and (scales == 127).any()       # clamp and all-zero blocks hit
