@@ -22,7 +22,10 @@ from tests import parity_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["fp4_mx_small", "fp8_mx_small", "fp4_small", "v3_small"]
+# fp4_odd_widths: shared widths that are not multiples of 128 (the shared gate|up
+# on the grouped kernel's dense form); *_decode: one-row-block tiles
+NAMES = ["fp4_mx_small", "fp8_mx_small", "fp4_small", "fp4_odd_widths", "fp4_mx_decode",
+         "fp8_mx_decode", "v3_small"]
 
 
 def _setup(name, dev):
