@@ -16,6 +16,7 @@ Prints one JSON line:
                bound, timed with HIP events on the library's stream
   cpu_baseline the float64 CPU oracle on a bounded sample of the same batch
   decode       the T=64 decode layer of the same weights (tokens/s, GB/s)
+  graph_ms_per_step  the same step replayed from a captured HIP graph
   aux_ops      the path's other calls: selection-bias step, FP4 -> FP8
                re-dequantisation, host tid2eid builders (beside the oracle's)
 """
@@ -224,6 +225,35 @@ def time_workload(wl, layer, steps, warmup, B, torch, cfg=None):
     views = B.workspace_views(cfg, T, ws)
     counts = views["counts"].cpu().numpy()
     return total_ms / steps, stage_ms, counts
+
+
+def time_graph(wl, layer, steps, B, torch, cfg=None):
+    """ms per replay of one forward captured in a HIP graph (torch.cuda.CUDAGraph),
+    the same call the timed steps make (second stream included): the launch
+    overhead the eager steps pay is what the two numbers differ by."""
+    cfg, T = (cfg or wl.cfg), wl.T
+    ws = B.alloc_workspace(cfg, T, layer["x"].device)
+    y = torch.empty_like(layer["x"])
+    side = side_stream(torch)
+    call = lambda: B.moe_forward_ex(cfg, layer, layer["x"], layer["token_ids"], T, y, ws,
+                                    side_stream=side)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del g, ws, y
+    return ms
 
 
 def workload_report(wl, ms, stage_ms, counts, peak):
@@ -468,6 +498,7 @@ def main():
     out["layer_roofline"] = {**rep["layer"], "mfma_frac": rep["layer_mfma_frac"],
                              "hbm_frac": rep["layer_hbm_frac"]}
     out["stage_ms"] = rep["stage_ms"]
+    out["graph_ms_per_step"] = round(time_graph(wl, rlayer, args.steps, B, torch, rcfg), 4)
 
     reports = {}
     names = ([args.decode] if args.decode else []) + [n for n in args.extra.split(",") if n]
@@ -485,10 +516,11 @@ def main():
         p2 = mfma_peak(w2.cfg)
         ms2, st2, c2 = time_workload(w2, l2, args.steps, args.warmup, B, torch, c2cfg)
         r2 = workload_report(w2, ms2, st2, c2, p2)
+        r2["graph_ms_per_step"] = round(time_graph(w2, l2, args.steps, B, torch, c2cfg), 4)
         r2["roofline"] = {k: r2["gemm1"][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
         r2["roofline"]["traffic"] = load_traffic(name, gemm_kind(w2.cfg))
         reports[name] = r2
-        log(f"{name}: {r2['ms_per_step']} ms/step, {r2['tokens_per_s']} tokens/s, stages {r2['stage_ms']}")
+        log(f"{name}: {r2['ms_per_step']} ms/step (graph {r2['graph_ms_per_step']}), {r2['tokens_per_s']} tokens/s, stages {r2['stage_ms']}")
         del l2
     if args.decode:
         out["decode"] = {"workload": args.decode, **reports.pop(args.decode)}
