@@ -345,7 +345,11 @@ int moe_permute(const moe_config *cfg, const int32_t *indices, int64_t T,
  *   ws  device workspace of at least moe_workspace_size(cfg, T) bytes,
  *       256-byte aligned; its sub-buffers (moe_ws_layout) hold the
  *       routing, permutation and intermediates of this call afterwards.
- * Everything is enqueued on `stream`; nothing persists between calls.
+ * Everything is enqueued on `stream`; nothing persists between calls.  The
+ * call enqueues only kernels (and, in the variants below, event records and
+ * waits): no host synchronisation, allocation or memset.  So it can be
+ * captured in a HIP graph and replayed; a replay reads x, the weights and the
+ * workspace at the addresses given at capture.
  * T == 0 is a no-op.  MOE_ERR_WORKSPACE if ws is NULL, misaligned or small. */
 int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                 const int32_t *token_ids, int64_t T, void *y,
