@@ -1,0 +1,109 @@
+"""GPU parity over seeded random layer configurations.
+
+The hand-picked workloads cover the pages' configurations and the edge cases.
+This module draws further valid configurations (moe_validate_config decides)
+to reach combinations nobody picked:
+- learned, hash or 2-gram routing; softmax, sigmoid or sqrt(softplus) scores;
+- groups, bias, renormalisation, route scale, the clamp and the shared expert;
+- bf16 or FP4 experts on bf16 or MXFP8 activations;
+- row or tiled weights, and token counts on both sides of the large-batch
+  paths.
+Each is checked against the oracle at the parity bars: routing and
+permutation bit-exact outside the near-tie band, outputs within 2e-2 (bf16)
+or 5e-2 (FP4).  The draws are fixed by their seeds."""
+
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_ffn_route_amd import binding as B
+from mixture_experts_ffn_route_amd import config as C
+from mixture_experts_ffn_route_amd import synth
+from tests import parity_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+N_DRAWS = 18
+
+
+def draw_workload(i):
+    """The i-th random workload (a valid configuration; resampled until valid)."""
+    rng = np.random.default_rng(9000 + i)
+    kind = ("bf16", "fp4", "mx")[i % 3]
+    mult = 64 if kind == "bf16" else 128
+    while True:
+        E = int(rng.choice([8, 16, 32, 48, 64, 96, 128, 256]))
+        G = int(rng.choice([g for g in (1, 2, 4, 8) if E % g == 0]))
+        route = str(rng.choice(["learned", "learned", "learned", "hash", "ngram"]))
+        k = int(rng.integers(1, min(E, 9) + 1))
+        cfg = C.MoEConfig(
+            dim=int(rng.integers(2, 6)) * mult,
+            n_routed_experts=E,
+            n_activated_experts=k,
+            moe_inter_dim=int(rng.integers(1, 4)) * mult,
+            n_expert_groups=G if route == "learned" else 1,
+            n_limited_groups=int(rng.integers(1, G + 1)) if route == "learned" else 1,
+            n_shared_experts=int(rng.integers(0, 2)),
+            score_func=str(rng.choice(["softmax", "sigmoid", "sqrtsoftplus"])),
+            route_scale=float(rng.choice([1.0, 1.5, 2.5])),
+            renormalize=int(rng.choice([-1, 0, 1])),
+            swiglu_limit=float(rng.choice([0.0, 10.0])),
+            route_mode=route,
+            vocab_size=int(rng.integers(300, 5000)) if route != "learned" else 0,
+            expert_dtype="bf16" if kind == "bf16" else "fp4",
+            has_bias=bool(rng.integers(0, 2)) and route == "learned",
+            act_quant="mxfp8" if kind == "mx" else "none")
+        if B.moe_validate_config(cfg) == B.MOE_OK:
+            break
+    T = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(1024, 1300))]))
+    x_scale = float(rng.choice([1.0, 20.0]))
+    if cfg.score_func == "sigmoid":
+        # scores of |z| ~ 20 round sigmoid to 1.0 in fp32: exact ties between
+        # many experts (settled by id) that the float64 oracle does not have
+        x_scale = 1.0
+    wl = C.Workload(f"draw{i}_{kind}", cfg, T=T, seed=100 + i, x_scale=x_scale,
+                    seq_len=int(rng.integers(16, 200)) if route == "ngram" else 0)
+    tiled = bool(rng.integers(0, 2))
+    return wl, tiled
+
+
+@pytest.mark.parametrize("i", range(N_DRAWS))
+def test_random_config_matches_oracle(i, gpu):
+    wl, tiled = draw_workload(i)
+    cfg, T = wl.cfg, wl.T
+    print(f"[random] {wl.name}: T={T} tiled={tiled} {cfg}", flush=True)
+    layer = synth.make_layer(wl, gpu)
+    ora_table = None
+    if cfg.route_mode == "hash":
+        table, _, _, _ = B.moe_build_tid2eid(layer["p"], cfg.n_routed_experts,
+                                             cfg.n_activated_experts)
+        ora_table, _, _, _ = oracle.tid2eid_greedy(layer["p"], cfg.n_routed_experts,
+                                                   cfg.n_activated_experts)
+        assert np.array_equal(table, ora_table)
+        layer["tid2eid"] = torch.from_numpy(table).to(gpu)
+    run_cfg, run_layer = B.pack_layer(cfg, layer) if tiled else (cfg, layer)
+    ws = B.alloc_workspace(run_cfg, T, gpu)
+    y = torch.empty_like(layer["x"])
+    B.moe_forward(run_cfg, run_layer, layer["x"], layer["token_ids"], T, y, ws)
+    torch.cuda.synchronize()
+
+    v = B.workspace_views(run_cfg, T, ws)
+    ow, oidx, aux = H.oracle_route(cfg, layer, ora_table)
+    gidx = H.cpu_np(v["route_indices"])
+    differ = H.compare_routing(cfg, H.cpu_np(v["route_weights"]), gidx, ow, oidx, aux)
+    counts, offsets = H.cpu_np(v["counts"]), H.cpu_np(v["offsets"])
+    st, ss, inv = H.cpu_np(v["sorted_tok"]), H.cpu_np(v["sorted_slot"]), H.cpu_np(v["inverse"])
+    H.check_permutation_valid(gidx, cfg.n_routed_experts, counts, offsets, st, ss, inv)
+    if not differ.any():
+        oc, _, ost, _, oinv = oracle.permute(oidx, cfg.n_routed_experts)
+        np.testing.assert_array_equal(counts, oc)
+        np.testing.assert_array_equal(st[:T * cfg.n_activated_experts], ost)
+        np.testing.assert_array_equal(inv, oinv)
+    keep = ~differ
+    yref = H.oracle_forward(cfg, H.f64(layer["x"])[keep], ow[keep], oidx[keep], layer)
+    err = H.max_rel_err(H.f64(y)[keep], yref)
+    print(f"[random] {wl.name}: max rel err {err:.3e}", flush=True)
+    assert err <= H.TOL["fp4" if cfg.expert_dtype == "fp4" else "bf16"]
+    assert int(v["flags"][0]) == 0
