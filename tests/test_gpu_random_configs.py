@@ -12,7 +12,6 @@ Each is checked against the oracle at the parity bars: routing and
 permutation bit-exact outside the near-tie band, outputs within 2e-2 (bf16)
 or 5e-2 (FP4).  The draws are fixed by their seeds."""
 
-
 import numpy as np
 import pytest
 import torch
