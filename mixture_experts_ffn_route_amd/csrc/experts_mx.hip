@@ -28,7 +28,6 @@
 //                       stored or FP8 weights re-dequantised from them
 //                       (redequant.hip).
 
-#include "fp8.h"
 #include "gemm.h"
 
 namespace moe {
@@ -36,7 +35,9 @@ namespace {
 
 // One thread per 32-input block (rows are contiguous, so block i of the
 // flattened array is row i / (K/32)): shared exponent floor(log2(amax)) - 8
-// clamped to [-127, 127] (0 for an all-zero block), codes of v / 2^X.
+// clamped to [-127, 127] (0 for an all-zero block), codes of v / 2^X by the
+// hardware E4M3 conversion (v_cvt_pk_fp8_f32: round to nearest, ties to even)
+// after clamping to +-448, which is the saturating OCP encoding.
 __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const bf16 *src, int64_t nblk,
                                                              uint8_t *codes, uint8_t *scales) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -63,10 +64,12 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const bf16 *src, in
   uint32_t w[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint32_t word = 0;
+    float q[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) word |= e4m3_code(ldexpf(v[4 * j + b], -X)) << (8 * b);
-    w[j] = word;
+    for (int b = 0; b < 4; ++b) q[b] = fminf(fmaxf(ldexpf(v[4 * j + b], -X), -448.f), 448.f);
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
+    w[j] = (uint32_t)word;
   }
   u32x4 *o = (u32x4 *)(codes + i * 32);
   o[0] = u32x4{w[0], w[1], w[2], w[3]};

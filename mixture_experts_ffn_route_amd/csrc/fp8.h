@@ -1,5 +1,5 @@
-// OCP 8-bit and 4-bit float helpers shared by the MXFP8 quantiser
-// (experts_mx.hip) and the FP4 -> FP8 re-dequantisation (redequant.hip).
+// OCP 8-bit and 4-bit float helpers of the FP4 -> FP8 re-dequantisation
+// (redequant.hip).
 //   E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; normals
 //         1.m x 2^(e-7) for e = 1..15 except the NaN codes S.1111.111,
 //         subnormals m/8 x 2^-6; largest finite 448.
