@@ -168,7 +168,9 @@ typedef struct {
   size_t xq_scales;            /* uint8 [T, dim/32] their E8M0 scales            */
   size_t hq;                   /* uint8 [T*k, I] MXFP8 codes of H's routed rows  */
   size_t hq_scales;            /* uint8 [T*k, I/32]                              */
-  size_t h;                    /* [T*k + T, I]   SwiGLU activations (bf16/f32)   */
+  size_t h;                    /* [T*k + T, I]   SwiGLU activations (bf16/f32);
+                                  MXFP8 layers may leave the routed rows unwritten
+                                  (the gate|up GEMM writes hq directly)          */
   size_t yrows;                /* [T*k + T, dim] weighted expert outputs         */
   int32_t max_tiles;
   int32_t tile_rows;           /* rows per GEMM tile chosen for this (cfg, T)    */

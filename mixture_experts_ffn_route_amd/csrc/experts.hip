@@ -703,10 +703,15 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
       if (!side && (err = launch_quantize_mxfp8((const bf16 *)p.x, p.T, p.dim, p.xq,
                                                 p.xq_scales, s)) != hipSuccess)
         return err;
+      // H's routed rows go straight to MXFP8 for the down GEMM
       a.Aq = p.xq;
       a.Asc = p.xq_scales;
+      a.Cq = p.hq;
+      a.Csc = p.hq_scales;
       if ((err = launch_gemm_mx(2, mb, a, p.max_tiles - p.n_shared_tiles, s)) != hipSuccess)
         return err;
+      a.Cq = nullptr;
+      a.Csc = nullptr;
     } else if ((err = gemm_launch(2, fp4, mb, a, p.max_tiles - p.n_shared_tiles, s)) !=
                hipSuccess) {
       return err;
@@ -736,9 +741,6 @@ hipError_t launch_experts(const ExpertPlan &p, hipStream_t s) {
     a.tile_begin = p.n_shared_tiles; a.tile_end = -1;
     if (p.mx) {
       // the routed rows of H (the first T*k) in MXFP8, in permuted order
-      if ((err = launch_quantize_mxfp8((const bf16 *)p.h, routed_rows, p.inter, p.hq,
-                                       p.hq_scales, s)) != hipSuccess)
-        return err;
       a.Aq = p.hq;
       a.Asc = p.hq_scales;
       if ((err = launch_gemm_mx(1, mb, a, p.max_tiles - p.n_shared_tiles, s)) != hipSuccess)

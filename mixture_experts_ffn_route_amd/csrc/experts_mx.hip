@@ -78,6 +78,17 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const bf16 *src, in
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// Maximum over the 16 lanes of a DPP row, left on each of them: quad permutes
+// (1,0,3,2) and (2,3,0,1), then the half-row and row mirrors -- VALU lane
+// moves that need no LDS crossbar and no wait.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
+  return v;
+}
+
 // One decode tile on the scaled MFMA: MBE 16-row blocks, NB weight matrices,
 // NCB 16-column blocks per wave and matrix.  SLOT = bytes per LDS ring slot
 // (activation units, then the scale region).
@@ -593,6 +604,55 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
 
   if constexpr (NB == 2) {
     const float L = g.limit;
+    auto swiglu = [&](float gv, float uv) {
+      if (L > 0.f) {
+        gv = fminf(gv, L);
+        uv = fminf(fmaxf(uv, -L), L);
+      }
+      return gv / (1.f + __expf(-gv)) * uv;
+    };
+    if (g.Cq) {
+      // SwiGLU output straight to MXFP8, as the quantiser would encode it
+      // (from the fp32 value, not its bf16 rounding): a 32-column block of a
+      // row is column blocks 2c and 2c+1 of the 16 lanes that share the row
+      // (a DPP row), so its amax is a 16-lane reduction.  Lane r16 keeps the
+      // scale of block r16 and the lanes of a row store the slab's scales at
+      // once.
+      static_assert(SC % 2 == 0 && SC <= 32, "whole MX blocks per slab");
+      const int64_t NS = N / 32;
+#pragma unroll
+      for (int m = 0; m < MW; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = (mb0 + m) * 16 + q * 4 + i;
+          const int64_t R = row0 + row;
+          uint8_t *qrow = g.Cq + R * N + col0 + r16;
+          int my_sc = 0;
+#pragma unroll
+          for (int c = 0; c < SC / 2; ++c) {
+            const float v0 = swiglu(acc[m][0][2 * c][i], acc[m][1][2 * c][i]);
+            const float v1 = swiglu(acc[m][0][2 * c + 1][i], acc[m][1][2 * c + 1][i]);
+            const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
+            int X = 0;
+            if (amax > 0.f) {
+              int ex;
+              frexpf(amax, &ex);               // amax = f * 2^ex, f in [0.5, 1)
+              X = ex - 1 - 8;
+              X = X < -127 ? -127 : (X > 127 ? 127 : X);
+            }
+            if (r16 == c) my_sc = X + 127;
+            const float q0 = fminf(fmaxf(ldexpf(v0, -X), -448.f), 448.f);
+            const float q1 = fminf(fmaxf(ldexpf(v1, -X), -448.f), 448.f);
+            const int word = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+            if (row < rows) {
+              qrow[32 * c] = (uint8_t)word;
+              qrow[32 * c + 16] = (uint8_t)(word >> 8);
+            }
+          }
+          if (row < rows && r16 < SC / 2) g.Csc[R * NS + col0 / 32 + r16] = (uint8_t)my_sc;
+        }
+      return;
+    }
 #pragma unroll
     for (int m = 0; m < MW; ++m)
 #pragma unroll
@@ -601,14 +661,8 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
         if (row < rows) {
           bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
 #pragma unroll
-          for (int cb = 0; cb < SC; ++cb) {
-            float gv = acc[m][0][cb][i], uv = acc[m][1][cb][i];
-            if (L > 0.f) {
-              gv = fminf(gv, L);
-              uv = fminf(fmaxf(uv, -L), L);
-            }
-            crow[cb * 16] = (bf16)(gv / (1.f + __expf(-gv)) * uv);
-          }
+          for (int cb = 0; cb < SC; ++cb)
+            crow[cb * 16] = (bf16)swiglu(acc[m][0][cb][i], acc[m][1][cb][i]);
         }
       }
   } else {
@@ -678,7 +732,7 @@ void grouped_gemm_mx_rs(const GemmArgs g) {
 
 template <int WAVES, int NB, int SC, int MB, int NSA, int NSB, int WPE, bool F8 = false>
 hipError_t run_gemm_mx_rs(GemmArgs a, int max_tiles, hipStream_t s) {
-  if (a.N % (SC * 16)) return hipErrorInvalidValue;
+  if (a.N % (SC * 16) || (a.Cq && (NB != 2 || !a.Csc))) return hipErrorInvalidValue;
   a.n_slabs = a.N / (SC * 16);
   const int64_t blocks = gemm_grid_blocks(a, max_tiles);
   if (blocks <= 0) return hipSuccess;
@@ -745,9 +799,15 @@ hipError_t run_gemm_mx_mb(GemmArgs a, int max_tiles, hipStream_t s) {
     if (a.N % (WIDE * 16) == 0) return run_gemm_mx_rs<4, NB, WIDE, MB, 3, 3, 1>(a, max_tiles, s);
     return run_gemm_mx_rs<4, NB, NARROW, MB, 3, 3, 1>(a, max_tiles, s);
   } else {
-    if (NB == 1 && a.N % 256 == 0) return run_gemm_mx<8, 1, 2, MB, 3, 2>(a, max_tiles, s);
-    if (a.N % 128 == 0) return run_gemm_mx<8, NB, 1, MB, 3, 2>(a, max_tiles, s);
-    return run_gemm_mx<4, NB, 1, MB, 3, 1>(a, max_tiles, s);     // N % 64 == 0
+    // the decode kernel writes bf16 C; an MXFP8 form asked for follows from it
+    GemmArgs d = a;
+    d.Cq = nullptr; d.Csc = nullptr;
+    hipError_t err;
+    if (NB == 1 && a.N % 256 == 0) err = run_gemm_mx<8, 1, 2, MB, 3, 2>(d, max_tiles, s);
+    else if (a.N % 128 == 0) err = run_gemm_mx<8, NB, 1, MB, 3, 2>(d, max_tiles, s);
+    else err = run_gemm_mx<4, NB, 1, MB, 3, 1>(d, max_tiles, s);     // N % 64 == 0
+    if (err != hipSuccess || !a.Cq) return err;
+    return launch_quantize_mxfp8(a.C, a.routed_rows, a.N, a.Cq, a.Csc, s);
   }
 }
 

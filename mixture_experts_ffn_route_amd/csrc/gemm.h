@@ -32,6 +32,8 @@ struct GemmArgs {
   int64_t routed_rows;       // T * k: rows at or above this belong to the shared expert
   int b_fp8;                 // MX form: B is E4M3 in the FP8 expert layout and S its
                              //   128 x 128 block scales [E, N/128, K/128]
+  uint8_t *Cq;               // two-matrix MX form: the SwiGLU output in MXFP8 instead
+  uint8_t *Csc;              //   of C -- E4M3 codes [*, N], E8M0 scales [*, N/32] -- or null
 };
 
 #define MOE_LDS __attribute__((address_space(3)))
@@ -128,6 +130,8 @@ inline int64_t gemm_grid_blocks(const GemmArgs &a, int max_tiles) {
 }
 
 // MX launches (experts_mx.hip): routed FP4 experts on MXFP8 activations.
+// With a.Cq set (gate|up only) the output is the MXFP8 form of the SwiGLU
+// rows 0 .. a.routed_rows-1; decode-height tiles also write them to a.C.
 hipError_t launch_gemm_mx(int nb, int mb, GemmArgs a, int max_tiles, hipStream_t s);
 // E4M3 codes + E8M0 scales (OCP MX, one scale per 32 inputs) of rows x K.
 hipError_t launch_quantize_mxfp8(const bf16 *src, int64_t rows, int K, uint8_t *codes,

@@ -276,3 +276,64 @@ def test_mxfp8_codes_on_edge_values(name, gpu):
     np.testing.assert_array_equal(H.cpu_np(v["xq_scales"]), scales)
     np.testing.assert_array_equal(H.cpu_np(v["xq"]), codes)
     assert (scales == 0).any() and (scales == 127).any()       # clamp and all-zero blocks hit
+
+
+@pytest.mark.parametrize("name", [n for n, w in C.SMALL_WORKLOADS.items()
+                                  if w.cfg.act_quant == "mxfp8"])
+def test_mxfp8_hidden_codes(name, gpu):
+    """The down GEMM's input: the routed rows of H in MXFP8, in permuted order.
+    The gate|up GEMM writes them from its fp32 SwiGLU values (decode-height FP4
+    tiles: the quantiser from bf16 H).  Against the oracle's float64 H of each
+    permuted row (its expert's gate and up on the oracle-quantised x, through
+    swiglu_expert with an identity down matrix):
+    - every shared exponent equals the oracle's, or differs by one where the
+      block maximum lies within 2^-7 relative of a power of two (the GEMM's
+      rounding can put it on either side);
+    - every decoded element equals the oracle's value, saturated at 448 times
+      the GPU's block scale, to within half an E4M3 step (2^-4 relative, 2^(X-10)
+      absolute below the normal range), the bf16 rounding of the decode-tile
+      path, and 1e-4 of the block maximum for the GEMM's fp32 sums."""
+    wl = C.SMALL_WORKLOADS[name]
+    cfg, T = wl.cfg, wl.T
+    k, I, E = cfg.n_activated_experts, cfg.moe_inter_dim, cfg.n_routed_experts
+    layer, _ = _layer(wl, gpu)
+    run_cfg, run_layer = H.run_weights(wl, cfg, layer, B)
+    ws = B.alloc_workspace(run_cfg, T, gpu)
+    y = torch.empty_like(layer["x"])
+    tile_rows = B.moe_workspace_layout(run_cfg, T)["tile_rows"]
+    print(f"[mx-hidden] {name} T={T} tile rows {tile_rows}", flush=True)
+    B.moe_forward(run_cfg, run_layer, layer["x"], layer["token_ids"], T, y, ws)
+    torch.cuda.synchronize()
+    v = B.workspace_views(run_cfg, T, ws)
+    hq, hs = H.cpu_np(v["hq"]), H.cpu_np(v["hq_scales"])
+    offsets, st = H.cpu_np(v["offsets"]), H.cpu_np(v["sorted_tok"])
+
+    xd = oracle.mxfp8_decode(*oracle.mxfp8_quantize(H.f64(layer["x"])))
+    get = H.expert_fetcher(layer, cfg, fp8=wl.fp8_weights)
+    eye = np.eye(I)
+    href = np.zeros((T * k, I))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            wg, wu, _ = get(e)
+            href[r0:r1] = oracle.swiglu_expert(xd[st[r0:r1]], wg, wu, eye, cfg.swiglu_limit)
+
+    _, osc = oracle.mxfp8_quantize(href)
+    amax = np.abs(href).reshape(T * k, I // 32, 32).max(axis=2)
+    with np.errstate(divide="ignore"):
+        rel = np.abs(amax / np.exp2(np.round(np.log2(np.where(amax > 0, amax, 1.0)))) - 1.0)
+    diff = hs.astype(np.int64) - osc.astype(np.int64)
+    assert np.all(np.abs(diff) <= 1)
+    assert np.all(rel[diff != 0] < 2.0 ** -7), "shared exponent off away from a power of two"
+    assert (diff != 0).mean() < 0.01
+
+    X = np.repeat(hs.astype(np.int64) - 127, 32, axis=1).astype(np.float64)
+    lim = 448.0 * np.exp2(X)
+    want = np.clip(href, -lim, lim)
+    dec = oracle.mxfp8_decode(hq, hs)
+    tol = ((2.0 ** -4 + 2.0 ** -8) * np.abs(want) + np.exp2(X - 10)
+           + 1e-4 * np.repeat(amax, 32, axis=1))
+    bad = np.abs(dec - want) > tol
+    print(f"[mx-hidden] {name}: {int((diff != 0).sum())} exponents off by one, "
+          f"{int(bad.sum())} elements out of bound", flush=True)
+    assert not bad.any()
