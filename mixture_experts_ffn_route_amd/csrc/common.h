@@ -57,4 +57,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float bf16_to_f32(bf16 v) { return (float)v; }
 
+// SwiGLU of one gate / up pair, with the clamp when L > 0 (gate capped at L,
+// up clamped to [-L, L]).  SiLU divides by the hardware reciprocal (v_rcp_f32,
+// 1 ulp) instead of the correctly rounded division sequence: the value is
+// rounded to bf16 or E4M3 right after, and 1 + e^-g >= 1 keeps the reciprocal
+// away from zero and denormals (e^-g = inf gives 0, the limit).
+__device__ __forceinline__ float swiglu_pair(float g, float u, float L) {
+  if (L > 0.f) {
+    g = fminf(g, L);
+    u = fminf(fmaxf(u, -L), L);
+  }
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
 }  // namespace moe

@@ -190,12 +190,7 @@ __device__ __forceinline__ void dense_tile(const DenseArgs &g, int64_t m0, int n
       for (int j = 0; j < 2; ++j) {
         const int64_t col = n0 + 64 * wc + 32 * j + r32;
         if constexpr (NB == 2) {
-          float gv = acc[i][0][j][e], uv = acc[i][1][j][e];
-          if (g.limit > 0.f) {
-            gv = fminf(gv, g.limit);
-            uv = fminf(fmaxf(uv, -g.limit), g.limit);
-          }
-          g.C[row * N + col] = (bf16)(gv / (1.f + __expf(-gv)) * uv);
+          g.C[row * N + col] = (bf16)swiglu_pair(acc[i][0][j][e], acc[i][1][j][e], g.limit);
         } else {
           g.Cf[((int64_t)part * M + row) * N + col] = acc[i][0][j][e];
         }

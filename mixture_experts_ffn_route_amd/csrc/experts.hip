@@ -266,15 +266,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
         if (row < rows) {
           bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            float gv = acc[m][0][cb][i], uv = acc[m][1][cb][i];
-            if (L > 0.f) {
-              gv = fminf(gv, L);
-              uv = fminf(fmaxf(uv, -L), L);
-            }
-            const float h = gv / (1.f + __expf(-gv)) * uv;
-            crow[cb * 16] = (bf16)h;
-          }
+          for (int cb = 0; cb < NCB; ++cb)
+            crow[cb * 16] = (bf16)swiglu_pair(acc[m][0][cb][i], acc[m][1][cb][i], L);
         }
       }
   } else {

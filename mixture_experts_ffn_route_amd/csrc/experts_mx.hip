@@ -284,14 +284,8 @@ __device__ __forceinline__ void gemm_tile_mx(const GemmArgs &g, const TileCtx &t
         if (row < rows) {
           bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            float gv = acc[m][0][cb][i], uv = acc[m][1][cb][i];
-            if (L > 0.f) {
-              gv = fminf(gv, L);
-              uv = fminf(fmaxf(uv, -L), L);
-            }
-            crow[cb * 16] = (bf16)(gv / (1.f + __expf(-gv)) * uv);
-          }
+          for (int cb = 0; cb < NCB; ++cb)
+            crow[cb * 16] = (bf16)swiglu_pair(acc[m][0][cb][i], acc[m][1][cb][i], L);
         }
       }
   } else {
@@ -604,13 +598,7 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
 
   if constexpr (NB == 2) {
     const float L = g.limit;
-    auto swiglu = [&](float gv, float uv) {
-      if (L > 0.f) {
-        gv = fminf(gv, L);
-        uv = fminf(fmaxf(uv, -L), L);
-      }
-      return gv / (1.f + __expf(-gv)) * uv;
-    };
+    auto swiglu = [&](float gv, float uv) { return swiglu_pair(gv, uv, L); };
     if (g.Cq) {
       // SwiGLU output straight to MXFP8, as the quantiser would encode it
       // (from the fp32 value, not its bf16 rounding): a 32-column block of a
