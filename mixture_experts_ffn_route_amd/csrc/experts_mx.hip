@@ -27,6 +27,9 @@
 //                       through LDS (gemm_tile_mx_rs below); FP4 weights as
 //                       stored or FP8 weights re-dequantised from them
 //                       (redequant.hip).
+// The down GEMM's input, H in MXFP8, comes from the row-split gate|up
+// epilogue directly; the decode kernel writes bf16 H and the quantiser
+// follows it.
 
 #include "gemm.h"
 
