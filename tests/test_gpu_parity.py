@@ -6,6 +6,8 @@ lie within 1e-6 relative; routing weights to 1e-5 relative; layer outputs
 max|y - y_ref| / max|y_ref| <= 2e-2 (bf16), 5e-2 (FP4), 1e-4 (fp32).
 """
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -278,9 +280,12 @@ def test_mxfp8_codes_on_edge_values(name, gpu):
     assert (scales == 0).any() and (scales == 127).any()       # clamp and all-zero blocks hit
 
 
-@pytest.mark.parametrize("name", [n for n, w in C.SMALL_WORKLOADS.items()
-                                  if w.cfg.act_quant == "mxfp8"])
-def test_mxfp8_hidden_codes(name, gpu):
+_MX_NAMES = [n for n, w in C.SMALL_WORKLOADS.items() if w.cfg.act_quant == "mxfp8"]
+
+
+@pytest.mark.parametrize("name,no_clamp", [(n, False) for n in _MX_NAMES] +
+                         [("fp4_mx_clamp", True), ("fp8_mx_clamp", True)])
+def test_mxfp8_hidden_codes(name, no_clamp, gpu):
     """The down GEMM's input: the routed rows of H in MXFP8, in permuted order.
     The gate|up GEMM writes them from its fp32 SwiGLU values (decode-height FP4
     tiles: the quantiser from bf16 H).  Against the oracle's float64 H of each
@@ -292,8 +297,13 @@ def test_mxfp8_hidden_codes(name, gpu):
     - every decoded element equals the oracle's value, saturated at 448 times
       the GPU's block scale, to within half an E4M3 step (2^-4 relative, 2^(X-10)
       absolute below the normal range), the bf16 rounding of the decode-tile
-      path, and 1e-4 of the block maximum for the GEMM's fp32 sums."""
+      path, and 1e-4 of the block maximum for the GEMM's fp32 sums.
+    no_clamp: the same layer without the SwiGLU clamp (x ~ N(0, 20^2), so H
+    reaches past the clamp's range), the layer output also checked against
+    the oracle."""
     wl = C.SMALL_WORKLOADS[name]
+    if no_clamp:
+        wl = replace(wl, cfg=replace(wl.cfg, swiglu_limit=0.0))
     cfg, T = wl.cfg, wl.T
     k, I, E = cfg.n_activated_experts, cfg.moe_inter_dim, cfg.n_routed_experts
     layer, _ = _layer(wl, gpu)
@@ -337,3 +347,13 @@ def test_mxfp8_hidden_codes(name, gpu):
     print(f"[mx-hidden] {name}: {int((diff != 0).sum())} exponents off by one, "
           f"{int(bad.sum())} elements out of bound", flush=True)
     assert not bad.any()
+    if no_clamp:
+        ow, oidx, aux = H.oracle_route(cfg, layer)
+        differ = H.compare_routing(cfg, H.cpu_np(v["route_weights"]), H.cpu_np(v["route_indices"]),
+                                   ow, oidx, aux)
+        keep = ~differ
+        yref = H.oracle_forward(cfg, H.f64(layer["x"])[keep], ow[keep], oidx[keep], layer,
+                                fp8=wl.fp8_weights)
+        err = H.max_rel_err(H.f64(y)[keep], yref)
+        print(f"[mx-hidden] {name} without the clamp: max rel err {err:.3e}", flush=True)
+        assert err <= H.TOL["fp4"]
