@@ -24,7 +24,7 @@ from tests import parity_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-N_DRAWS = 18
+N_DRAWS = 36
 
 
 def draw_workload(i):
