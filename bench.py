@@ -98,7 +98,7 @@ def algorithmic_counts(wl, counts):
 
 def achievable_peaks(torch, B):
     """Achievable denominators on this GPU, from the library's roofline probes
-    (the layer kernels' own instruction forms): 16-byte loads streaming a
+    (the layer kernels' own instruction forms): 16-byte nontemporal loads streaming a
     4 GiB buffer, and chains of 16x16x32 bf16 MFMAs on every SIMD."""
     dev = torch.device("cuda:0")
     buf = torch.empty(1 << 32, dtype=torch.uint8, device=dev)

@@ -401,7 +401,7 @@ int moe_forward_ex(const moe_config *cfg, const moe_weights *w, const void *x,
 
 /* Roofline probes: the achievable HBM read rate and bf16 MFMA rate of the
  * GPU, measured with the instruction forms the layer kernels use (16-byte
- * vector loads; v_mfma_f32_16x16x32_bf16), for the caller to time on
+ * nontemporal vector loads; v_mfma_f32_16x16x32_bf16), for the caller to time on
  * `stream` and report next to the data-sheet peaks.  Neither touches the
  * layer state.
  *   moe_probe_read: reads `bytes` (a multiple of 16) of `buf` (16-byte

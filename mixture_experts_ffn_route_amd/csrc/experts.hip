@@ -41,7 +41,10 @@ namespace moe {
 // k-step s) is 64 lanes x 16 bytes, row 16m + (lane & 15) of the gathered
 // activations, so the LDS block already has the MFMA A-operand layout and the
 // readers take 16 consecutive bytes per lane without bank conflicts -- and
-// (b) its own weight columns as 16-byte loads into a register ring.  Stage st
+// (b) its own weight columns as 16-byte loads into a register ring
+// (bf16 weights: nontemporal in decode-height tiles, whose weights nothing
+// re-reads: V3 decode GEMM1 2.15 -> 1.96 ms; taller tiles keep plain loads,
+// which measured faster there).  Stage st
 // is consumed NS-1 stages after it was issued; one vmcnt wait and one barrier
 // per stage.
 template <int WAVES, int NB, int NCB, int MBE, bool FP4, int NS, int SLOT>
@@ -175,7 +178,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
         sq[SL][b][cb] = sptr[b][cb][ST * sst];
     } else {
       const int r = q - NFW, bc = r / NQ, qq = r - bc * NQ, b = bc / NCB, cb = bc - b * NCB;
-      bq[SL][b][cb][qq] = *(const u32x4 *)(bptr[b][cb] + ST * bst + qq * qst);
+      const u32x4 *src = (const u32x4 *)(bptr[b][cb] + ST * bst + qq * qst);
+      bq[SL][b][cb][qq] = MBE == 1 ? __builtin_nontemporal_load(src) : *src;
     }
   };
   auto issue_stage = [&](int SL, int ST) {
@@ -400,6 +404,8 @@ __global__ __launch_bounds__(256) void expert_down_f32(
 // permuted rows (and its shared row) are looked up first; then every lane
 // issues all k+1 16-byte loads of its chunk before adding them in slot order,
 // shared row last (a dropped pair, inverse = -1, contributes nothing).
+// Y is read once and y written once, so both go through nontemporal
+// accesses (0.114 -> 0.102 ms at the V3 prefill shape).
 template <int KMAX>
 __global__ __launch_bounds__(1024) void combine_bf16(const bf16 *__restrict__ Y,
                                                      const int32_t *__restrict__ inverse,
@@ -419,7 +425,8 @@ __global__ __launch_bounds__(1024) void combine_bf16(const bf16 *__restrict__ Y,
   for (int c = threadIdx.x * 8; c < dim; c += blockDim.x * 8) {
     bf16x8 v[KMAX + 1];
 #pragma unroll
-    for (int j = 0; j <= KMAX; ++j) v[j] = *(const bf16x8 *)(Y + row[j] * dim + c);
+    for (int j = 0; j <= KMAX; ++j)
+      v[j] = __builtin_nontemporal_load((const bf16x8 *)(Y + row[j] * dim + c));
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j <= KMAX; ++j)
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(1024) void combine_bf16(const bf16 *__restrict__ Y,
     bf16x8 o;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = (bf16)acc[i];
-    *(bf16x8 *)(y + t * dim + c) = o;
+    __builtin_nontemporal_store(o, (bf16x8 *)(y + t * dim + c));
   }
 }
 

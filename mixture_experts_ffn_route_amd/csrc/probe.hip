@@ -10,7 +10,9 @@ namespace moe {
 namespace {
 
 // Each wave streams its own contiguous 1/(4*grid) of the buffer, 1 KB per
-// load instruction and eight instructions in flight; the loaded words feed a
+// nontemporal load instruction (the form decode-height GEMM tiles stream
+// their weights with, and the faster one for a pure stream) and eight
+// instructions in flight; the loaded words feed a
 // value that is stored only if it matches a constant, so no load is dead.
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4 *p, int64_t n16,
                                                          uint32_t *out) {
@@ -24,7 +26,7 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4 *p, int64_t
   for (; k + 7 * 64 < per; k += 8 * 64) {
     u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = q[k + u * 64];
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(q + k + u * 64);
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u][u & 3];
   }
