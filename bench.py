@@ -343,67 +343,99 @@ def aux_ops(torch, B, dev, synth, C):
     return out
 
 
-def cpu_baseline(wl, layer, sample_tokens):
-    """The float64 oracle, as it is, on the first `sample_tokens` tokens:
-    routing + permutation + routed/shared SwiGLU forward."""
+# Tokens of each workload the CPU oracle is timed on: whole batches where the
+# oracle finishes them in seconds (the fp32 layer, the T=64 decode batch, the
+# hash layers), else the first tokens of the batch (the oracle's cost is the
+# experts those tokens touch, each widened to float64 at use).
+CPU_SAMPLE = {"tiny_fp32": None, "v3_decode": None, "hash_bf16": None, "ngram_bf16": None,
+              "v3_prefill": 96, "v41_flash_fp4": 16, "v41_flash_fp4_mx": 16,
+              "v41_flash_fp8": 8}
+
+
+def cpu_baseline(wl, layer, sample_tokens=None):
+    """The float64 oracle, as it is, on the first `sample_tokens` tokens (all
+    when None): routing + permutation + routed/shared SwiGLU forward (MXFP8
+    activations for the MXFP8 layers).  The experts the sample touches are
+    staged on the host in their stored format first (untimed; for the
+    FP8-weight layer that format is the oracle's own FP4 -> FP8
+    re-dequantisation, a load-time conversion like the GPU's, run in worker
+    processes); their widening to float64 is the oracle's work and is timed."""
     import numpy as np
     import torch
     import oracle
     from threadpoolctl import threadpool_info
 
     cfg = wl.cfg
-    S = min(sample_tokens, wl.T)
+    S = wl.T if sample_tokens is None else min(sample_tokens, wl.T)
     f32 = lambda t: t.detach().float().cpu().numpy()
     x = f32(layer["x"][:S])
+    ids = None if layer.get("token_ids") is None else layer["token_ids"][:S].cpu().numpy()
     table = None
     if cfg.route_mode == "hash":
         table, _, _, _ = oracle.tid2eid_greedy(layer["p"], cfg.n_routed_experts,
                                                cfg.n_activated_experts)
-        ids = layer["token_ids"][:S].cpu().numpy()
-        _, idx = oracle.hash_gate(ids, table, cfg.route_scale)
-    else:
-        bias = None if layer["gate_bias"] is None else layer["gate_bias"].cpu().numpy()
-        gate_w = f32(layer["gate_w"])
-        _, idx, _ = oracle.learned_gate(x, gate_w, bias, score_func=cfg.score_func,
-                                        n_groups=cfg.n_expert_groups,
-                                        topk_groups=cfg.n_limited_groups,
-                                        topk=cfg.n_activated_experts, route_scale=cfg.route_scale)
-    # host copies of the experts the sample touches, in their stored format
-    # (data staging, untimed; the widening to float64 is the oracle's work)
+    bias = None if layer.get("gate_bias") is None else layer["gate_bias"].cpu().numpy()
+    gate_w = f32(layer["gate_w"]) if cfg.route_mode == "learned" else None
+
+    def route():
+        if cfg.route_mode == "hash":
+            return oracle.hash_gate(ids, table, cfg.route_scale)
+        if cfg.route_mode == "ngram":
+            return oracle.ngram_hash_gate(ids[:, 0], ids[:, 1], cfg.vocab_size,
+                                          cfg.n_routed_experts, cfg.n_activated_experts,
+                                          cfg.route_scale)
+        w, i, _ = oracle.learned_gate(x, gate_w, bias, score_func=cfg.score_func,
+                                      n_groups=cfg.n_expert_groups,
+                                      topk_groups=cfg.n_limited_groups,
+                                      topk=cfg.n_activated_experts, route_scale=cfg.route_scale,
+                                      renormalize=cfg.renormalize)
+        return w, i
+
+    _, idx = route()
+    mats = ("w_gate", "w_up", "w_down")
     host = {}
-    for e in np.unique(idx):
-        e = int(e)
-        if cfg.expert_dtype == "fp4":
+    touched = [int(e) for e in np.unique(idx)]
+    if wl.fp8_weights:
+        import multiprocessing
+        from concurrent.futures import ProcessPoolExecutor
+        with ProcessPoolExecutor(16, mp_context=multiprocessing.get_context("spawn")) as pool:
+            futs = {e: [pool.submit(oracle.fp4_to_fp8_blocks, layer[n][e].cpu().numpy(),
+                                    layer["s_" + n[2:]][e].cpu().numpy()) for n in mats]
+                    for e in touched}
+            for e in touched:
+                host[e] = tuple(f.result()[:2] for f in futs[e])
+    elif cfg.expert_dtype == "fp4":
+        for e in touched:
             host[e] = tuple((layer[n][e].cpu().numpy(), layer["s_" + n[2:]][e].cpu().numpy())
-                            for n in ("w_gate", "w_up", "w_down"))
-        else:
-            host[e] = tuple(layer[n][e].cpu() for n in ("w_gate", "w_up", "w_down"))
-    shared = None
+                            for n in mats)
+    else:
+        for e in touched:
+            host[e] = tuple(layer[n][e].cpu() for n in mats)
+    shared_host = None
     if cfg.n_shared_experts:
         shared_host = tuple(layer[n].cpu() for n in ("sh_gate", "sh_up", "sh_down"))
 
     def expert(e):
+        if wl.fp8_weights:
+            return tuple(oracle.fp8_blocks_decode(c, b) for c, b in host[e])
         if cfg.expert_dtype == "fp4":
             return tuple(oracle.fp4_decode(p, s) for p, s in host[e])
         return tuple(a.double().numpy() for a in host[e])
 
+    forward = oracle.layer_forward_mx if cfg.act_quant == "mxfp8" else oracle.layer_forward
     t0 = time.perf_counter()
-    if cfg.route_mode == "hash":
-        w, idx = oracle.hash_gate(layer["token_ids"][:S].cpu().numpy(), table, cfg.route_scale)
-    else:
-        w, idx, _ = oracle.learned_gate(x, gate_w, bias, score_func=cfg.score_func,
-                                        n_groups=cfg.n_expert_groups,
-                                        topk_groups=cfg.n_limited_groups,
-                                        topk=cfg.n_activated_experts, route_scale=cfg.route_scale)
+    w, idx = route()
     oracle.permute(idx, cfg.n_routed_experts)
-    if cfg.n_shared_experts:
+    shared = None
+    if shared_host is not None:
         shared = tuple(a.double().numpy() for a in shared_host)
-    oracle.layer_forward(x, w, idx, expert, shared, cfg.swiglu_limit)
+    forward(x, w, idx, expert, shared, cfg.swiglu_limit)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [torch.get_num_threads()])
+    what = "all" if S == wl.T else f"the first {S} of the"
     return {"value": round(S / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {S} of the {wl.T} tokens of {wl.name}: route + permute + routed and "
-                      f"shared SwiGLU in float64 ({len(host)} experts touched), {dt:.1f} s"}
+            "sample": f"{what} {wl.T} tokens of {wl.name}: route + permute + routed and shared "
+                      f"SwiGLU in float64 ({len(host)} experts touched), {dt:.1f} s"}
 
 
 def main():
@@ -416,8 +448,9 @@ def main():
     ap.add_argument("--extra", default="hash_bf16,ngram_bf16,v41_flash_fp4,v41_flash_fp4_mx,"
                                       "v41_flash_fp8,tiny_fp32",
                     help="comma-separated further workloads to report ('' for none)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=96,
-                    help="tokens of the batch the CPU oracle is timed on (about 10 s)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=CPU_SAMPLE["v3_prefill"],
+                    help="tokens of the headline batch the CPU oracle is timed on (about 10 s); "
+                         "the other workloads use their CPU_SAMPLE entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the achievable matmul / HBM-read denominators and "
@@ -510,18 +543,24 @@ def main():
             l2 = dict(rlayer)
             l2["x"] = layer["x"][:w2.T].contiguous()
             c2cfg = rcfg
+            l2_src = dict(layer, x=l2["x"])
         else:
             log(f"generating {name} inputs")
-            c2cfg, l2 = run_weights(w2, build_layer(w2, dev, B, synth), B, args.layout)
+            l2_src = build_layer(w2, dev, B, synth)
+            c2cfg, l2 = run_weights(w2, l2_src, B, args.layout)
         p2 = mfma_peak(w2.cfg)
         ms2, st2, c2 = time_workload(w2, l2, args.steps, args.warmup, B, torch, c2cfg)
         r2 = workload_report(w2, ms2, st2, c2, p2)
         r2["graph_ms_per_step"] = round(time_graph(w2, l2, args.steps, B, torch, c2cfg), 4)
         r2["roofline"] = {k: r2["gemm1"][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
         r2["roofline"]["traffic"] = load_traffic(name, gemm_kind(w2.cfg))
+        if not args.no_cpu_baseline:
+            log(f"{name}: timing the CPU oracle")
+            r2["cpu_baseline"] = cpu_baseline(w2, l2_src, CPU_SAMPLE.get(name, 16))
+            log(f"{name}: cpu_baseline {r2['cpu_baseline']}")
         reports[name] = r2
         log(f"{name}: {r2['ms_per_step']} ms/step (graph {r2['graph_ms_per_step']}), {r2['tokens_per_s']} tokens/s, stages {r2['stage_ms']}")
-        del l2
+        del l2, l2_src
     if args.decode:
         out["decode"] = {"workload": args.decode, **reports.pop(args.decode)}
     if reports:

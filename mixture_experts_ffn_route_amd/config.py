@@ -149,6 +149,12 @@ SMALL_WORKLOADS = {
         replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=256, n_routed_experts=48,
                 act_quant="mxfp8"),
         T=9, description="MXFP8 activations, decode batch: one-row-block tiles"),
+    "fp4_mx_decode_narrow": Workload(
+        "fp4_mx_decode_narrow",
+        replace(V41_FLASH_FP4.cfg, dim=256, moe_inter_dim=384, n_routed_experts=48,
+                act_quant="mxfp8"),
+        T=9, description="MXFP8 activations, decode batch, a gate|up width that is a "
+                         "multiple of 128 but not of 256 (4-wave decode kernel)"),
     "fp4_mx_clamp": Workload(
         "fp4_mx_clamp",
         replace(V41_FLASH_FP4.cfg, dim=384, moe_inter_dim=256, n_routed_experts=24,

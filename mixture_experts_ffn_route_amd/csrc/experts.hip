@@ -527,34 +527,42 @@ static hipError_t run_gemm_mb(int mb, const GemmArgs &a, int max_tiles, hipStrea
 static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tiles,
                               hipStream_t s) {
   const bool decode = mb == 1;
+  // MOE_TRY: any tile height; MOE_TRY_DECODE: tiles of one row block only (the
+  // decode configurations are built for that height alone)
 #define MOE_TRY(W, NB_, NCB, FP4_, NS)                                          \
   if (a.N % ((W) * (NCB) * 16) == 0) {                                          \
     a.n_slabs = a.N / ((W) * (NCB) * 16);                                       \
     return run_gemm_mb<W, NB_, NCB, FP4_, NS>(mb, a, max_tiles, s);             \
   }
+#define MOE_TRY_DECODE(W, NB_, NCB, FP4_, NS)                                   \
+  if (a.N % ((W) * (NCB) * 16) == 0) {                                          \
+    a.n_slabs = a.N / ((W) * (NCB) * 16);                                       \
+    return run_gemm<W, NB_, NCB, 1, FP4_, NS>(a, max_tiles, s);                 \
+  }
   if (nb == 2) {
     if (fp4) {
-      if (decode) { MOE_TRY(4, 2, 2, true, 4) }
+      if (decode) { MOE_TRY_DECODE(4, 2, 2, true, 4) }
       else { MOE_TRY(8, 2, 1, true, 3) }
       MOE_TRY(4, 2, 1, true, 3)
     } else {
-      if (decode) { MOE_TRY(4, 2, 1, false, 4) }
+      if (decode) { MOE_TRY_DECODE(4, 2, 1, false, 4) }
       else if (mb >= 16) { MOE_TRY(8, 2, 1, false, 4) }
       else { MOE_TRY(8, 2, 1, false, 3) }
       MOE_TRY(4, 2, 1, false, 3)
     }
   } else {
     if (fp4) {
-      if (decode) { MOE_TRY(4, 1, 4, true, 4) }
+      if (decode) { MOE_TRY_DECODE(4, 1, 4, true, 4) }
       else { MOE_TRY(8, 1, 2, true, 3) }
       MOE_TRY(4, 1, 1, true, 3)
     } else {
-      if (decode) { MOE_TRY(4, 1, 2, false, 4) }
+      if (decode) { MOE_TRY_DECODE(4, 1, 2, false, 4) }
       else { MOE_TRY(8, 1, 2, false, 3) }
       MOE_TRY(4, 1, 1, false, 3)
     }
   }
 #undef MOE_TRY
+#undef MOE_TRY_DECODE
   return hipErrorInvalidValue;
 }
 

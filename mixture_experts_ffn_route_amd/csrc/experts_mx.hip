@@ -27,9 +27,9 @@
 //                       through LDS (gemm_tile_mx_rs below); FP4 weights as
 //                       stored or FP8 weights re-dequantised from them
 //                       (redequant.hip).
-// The down GEMM's input, H in MXFP8, comes from the row-split gate|up
-// epilogue directly; the decode kernel writes bf16 H and the quantiser
-// follows it.
+// The down GEMM's input, H in MXFP8, comes from the gate|up epilogues of
+// both forms directly (store_swiglu_mxfp8), encoded from the fp32 SwiGLU
+// values.
 
 #include "gemm.h"
 
@@ -97,6 +97,56 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
   return v;
+}
+
+// SwiGLU output rows straight to MXFP8, as the quantiser would encode them
+// (from the fp32 values, not their bf16 rounding).  acc holds MW row blocks
+// (the first is row block mb0 of the tile) x SC 16-column blocks of gate and
+// of up, in the 16x16 MFMA accumulator layout: lane (r16, q) has column
+// col0 + 16cb + r16 of rows 4q .. 4q+3.  A 32-column block of a row is column
+// blocks 2c and 2c+1 of the 16 lanes that share the row (a DPP row), so its
+// amax is a 16-lane reduction; lane r16 keeps the scale of block r16 and the
+// lanes of a row store the slab's scales at once.  Every lane takes part in
+// the reductions (rows past the tile hold finite padding values and are not
+// stored).
+template <int MW, int SC>
+__device__ __forceinline__ void store_swiglu_mxfp8(const GemmArgs &g, const f32x4 (&gate)[MW][SC],
+                                                   const f32x4 (&up)[MW][SC], int mb0, int row0,
+                                                   int rows, int col0, int N, int r16, int q) {
+  static_assert(SC % 2 == 0 && SC <= 32, "whole MX blocks per slab");
+  const float L = g.limit;
+  const int64_t NS = N / 32;
+#pragma unroll
+  for (int m = 0; m < MW; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (mb0 + m) * 16 + q * 4 + i;
+      const int64_t R = row0 + row;
+      uint8_t *qrow = g.Cq + R * N + col0 + r16;
+      int my_sc = 0;
+#pragma unroll
+      for (int c = 0; c < SC / 2; ++c) {
+        const float v0 = swiglu_pair(gate[m][2 * c][i], up[m][2 * c][i], L);
+        const float v1 = swiglu_pair(gate[m][2 * c + 1][i], up[m][2 * c + 1][i], L);
+        const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
+        int X = 0;
+        if (amax > 0.f) {
+          int ex;
+          frexpf(amax, &ex);                   // amax = f * 2^ex, f in [0.5, 1)
+          X = ex - 1 - 8;
+          X = X < -127 ? -127 : (X > 127 ? 127 : X);
+        }
+        if (r16 == c) my_sc = X + 127;
+        const float q0 = fminf(fmaxf(ldexpf(v0, -X), -448.f), 448.f);
+        const float q1 = fminf(fmaxf(ldexpf(v1, -X), -448.f), 448.f);
+        const int word = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+        if (row < rows) {
+          qrow[32 * c] = (uint8_t)word;
+          qrow[32 * c + 16] = (uint8_t)(word >> 8);
+        }
+      }
+      if (row < rows && r16 < SC / 2) g.Csc[R * NS + col0 / 32 + r16] = (uint8_t)my_sc;
+    }
 }
 
 // One decode tile on the scaled MFMA: MBE 16-row blocks, NB weight matrices,
@@ -285,6 +335,20 @@ __device__ __forceinline__ void gemm_tile_mx(const GemmArgs &g, const TileCtx &t
 
   // ---- epilogue (accumulator layout of the 16x16 MFMA forms) ----
   if constexpr (NB == 2) {
+    if constexpr (NCB % 2 == 0) {
+      if (g.Cq) {
+        f32x4 gate[MBE][NCB], up[MBE][NCB];
+#pragma unroll
+        for (int m = 0; m < MBE; ++m)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            gate[m][cb] = acc[m][0][cb];
+            up[m][cb] = acc[m][1][cb];
+          }
+        store_swiglu_mxfp8<MBE, NCB>(g, gate, up, 0, row0, rows, col0, N, r16, q);
+        return;
+      }
+    }
     const float L = g.limit;
 #pragma unroll
     for (int m = 0; m < MBE; ++m)
@@ -613,45 +677,15 @@ __device__ __forceinline__ void gemm_tile_mx_rs(const GemmArgs &g, const TileCtx
     const float L = g.limit;
     auto swiglu = [&](float gv, float uv) { return swiglu_pair(gv, uv, L); };
     if (g.Cq) {
-      // SwiGLU output straight to MXFP8, as the quantiser would encode it
-      // (from the fp32 value, not its bf16 rounding): a 32-column block of a
-      // row is column blocks 2c and 2c+1 of the 16 lanes that share the row
-      // (a DPP row), so its amax is a 16-lane reduction.  Lane r16 keeps the
-      // scale of block r16 and the lanes of a row store the slab's scales at
-      // once.
-      static_assert(SC % 2 == 0 && SC <= 32, "whole MX blocks per slab");
-      const int64_t NS = N / 32;
+      f32x4 gate[MW][SC], up[MW][SC];
 #pragma unroll
       for (int m = 0; m < MW; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = (mb0 + m) * 16 + q * 4 + i;
-          const int64_t R = row0 + row;
-          uint8_t *qrow = g.Cq + R * N + col0 + r16;
-          int my_sc = 0;
-#pragma unroll
-          for (int c = 0; c < SC / 2; ++c) {
-            const float v0 = swiglu(acc[m][0][2 * c][i], acc[m][1][2 * c][i]);
-            const float v1 = swiglu(acc[m][0][2 * c + 1][i], acc[m][1][2 * c + 1][i]);
-            const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
-            int X = 0;
-            if (amax > 0.f) {
-              int ex;
-              frexpf(amax, &ex);               // amax = f * 2^ex, f in [0.5, 1)
-              X = ex - 1 - 8;
-              X = X < -127 ? -127 : (X > 127 ? 127 : X);
-            }
-            if (r16 == c) my_sc = X + 127;
-            const float q0 = fminf(fmaxf(ldexpf(v0, -X), -448.f), 448.f);
-            const float q1 = fminf(fmaxf(ldexpf(v1, -X), -448.f), 448.f);
-            const int word = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-            if (row < rows) {
-              qrow[32 * c] = (uint8_t)word;
-              qrow[32 * c + 16] = (uint8_t)(word >> 8);
-            }
-          }
-          if (row < rows && r16 < SC / 2) g.Csc[R * NS + col0 / 32 + r16] = (uint8_t)my_sc;
+        for (int cb = 0; cb < SC; ++cb) {
+          gate[m][cb] = acc[m][0][cb];
+          up[m][cb] = acc[m][1][cb];
         }
+      store_swiglu_mxfp8<MW, SC>(g, gate, up, mb0, row0, rows, col0, N, r16, q);
       return;
     }
 #pragma unroll
@@ -800,15 +834,17 @@ hipError_t run_gemm_mx_mb(GemmArgs a, int max_tiles, hipStream_t s) {
     if (a.N % (WIDE * 16) == 0) return run_gemm_mx_rs<4, NB, WIDE, MB, 3, 3, 1>(a, max_tiles, s);
     return run_gemm_mx_rs<4, NB, NARROW, MB, 3, 3, 1>(a, max_tiles, s);
   } else {
-    // the decode kernel writes bf16 C; an MXFP8 form asked for follows from it
-    GemmArgs d = a;
-    d.Cq = nullptr; d.Csc = nullptr;
-    hipError_t err;
-    if (NB == 1 && a.N % 256 == 0) err = run_gemm_mx<8, 1, 2, MB, 3, 2>(d, max_tiles, s);
-    else if (a.N % 128 == 0) err = run_gemm_mx<8, NB, 1, MB, 3, 2>(d, max_tiles, s);
-    else err = run_gemm_mx<4, NB, 1, MB, 3, 1>(d, max_tiles, s);     // N % 64 == 0
-    if (err != hipSuccess || !a.Cq) return err;
-    return launch_quantize_mxfp8(a.C, a.routed_rows, a.N, a.Cq, a.Csc, s);
+    // decode tiles; gate|up with an MXFP8 output: two 16-column blocks of
+    // each matrix per wave, so that every 32-column MX block of a row lies in
+    // one wave (N % 128 == 0 on MXFP8 layers)
+    if (a.Cq) {
+      if (NB != 2 || !a.Csc || a.N % 128 != 0) return hipErrorInvalidValue;
+      if (a.N % 256 == 0) return run_gemm_mx<8, 2, 2, MB, 3, 2>(a, max_tiles, s);
+      return run_gemm_mx<4, 2, 2, MB, 3, 2>(a, max_tiles, s);
+    }
+    if (NB == 1 && a.N % 256 == 0) return run_gemm_mx<8, 1, 2, MB, 3, 2>(a, max_tiles, s);
+    if (a.N % 128 == 0) return run_gemm_mx<8, NB, 1, MB, 3, 2>(a, max_tiles, s);
+    return run_gemm_mx<4, NB, 1, MB, 3, 1>(a, max_tiles, s);     // N % 64 == 0
   }
 }
 

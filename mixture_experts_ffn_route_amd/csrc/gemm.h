@@ -131,7 +131,7 @@ inline int64_t gemm_grid_blocks(const GemmArgs &a, int max_tiles) {
 
 // MX launches (experts_mx.hip): routed FP4 experts on MXFP8 activations.
 // With a.Cq set (gate|up only) the output is the MXFP8 form of the SwiGLU
-// rows 0 .. a.routed_rows-1; decode-height tiles also write them to a.C.
+// rows 0 .. a.routed_rows-1 (a.C is not written).
 hipError_t launch_gemm_mx(int nb, int mb, GemmArgs a, int max_tiles, hipStream_t s);
 // E4M3 codes + E8M0 scales (OCP MX, one scale per 32 inputs) of rows x K.
 hipError_t launch_quantize_mxfp8(const bf16 *src, int64_t rows, int K, uint8_t *codes,

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -133,28 +134,68 @@ int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Events that fork a caller's side stream from its main stream and join it
-// back: three per host thread and device, created on the thread's first call
-// with a side stream on that device and kept until the process ends.  A
-// thread enqueues its calls one after another, and a wait takes the record
-// made just before it, so the next call may record the same events again;
-// no other thread uses them.
+// back: three per host thread and device.  A thread takes a triple for a
+// device on its first call with a side stream there and keeps it while it
+// lives; when the thread ends, its triples go back to a process-wide pool for
+// the next thread that needs one (no HIP call at thread or process exit), so
+// the number of events is bounded by the threads alive at once, not by the
+// threads ever created.  A thread enqueues its calls one after another, and a
+// wait takes the record made just before it, so the next call may record the
+// same events again; no other thread uses them while they are taken.
 struct SideEvents {
   hipEvent_t fork = nullptr, join = nullptr, xq_ready = nullptr;
+  int device = -1;
 };
 constexpr int kMaxDevices = 64;
 
+std::mutex &side_pool_mutex() {
+  static std::mutex *m = new std::mutex;       // never destroyed: used at thread exit
+  return *m;
+}
+std::vector<SideEvents> &side_pool() {
+  static std::vector<SideEvents> *v = new std::vector<SideEvents>;
+  return *v;
+}
+
+struct ThreadSideEvents {
+  SideEvents per_device[kMaxDevices];
+  ~ThreadSideEvents() {
+    std::lock_guard<std::mutex> lock(side_pool_mutex());
+    for (const SideEvents &ev : per_device)
+      if (ev.device >= 0) side_pool().push_back(ev);
+  }
+};
+
 hipError_t side_events(SideEvents **out) {
-  thread_local SideEvents per_device[kMaxDevices];
+  thread_local ThreadSideEvents mine;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  SideEvents &ev = per_device[dev];
-  if (!ev.xq_ready) {
-    SideEvents n;
-    for (hipEvent_t *p : {&n.fork, &n.join, &n.xq_ready})
-      if ((e = hipEventCreateWithFlags(p, hipEventDisableTiming)) != hipSuccess) return e;
-    ev = n;
+  SideEvents &ev = mine.per_device[dev];
+  if (ev.device < 0) {
+    {
+      std::lock_guard<std::mutex> lock(side_pool_mutex());
+      std::vector<SideEvents> &pool = side_pool();
+      for (size_t i = 0; i < pool.size(); ++i)
+        if (pool[i].device == dev) {
+          ev = pool[i];
+          pool.erase(pool.begin() + (std::ptrdiff_t)i);
+          break;
+        }
+    }
+    if (ev.device < 0) {
+      SideEvents n;
+      for (hipEvent_t *p : {&n.fork, &n.join, &n.xq_ready}) {
+        if ((e = hipEventCreateWithFlags(p, hipEventDisableTiming)) != hipSuccess) {
+          for (hipEvent_t q : {n.fork, n.join, n.xq_ready})
+            if (q) (void)hipEventDestroy(q);
+          return e;
+        }
+      }
+      n.device = dev;
+      ev = n;
+    }
   }
   *out = &ev;
   return hipSuccess;
@@ -437,24 +478,38 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   hipError_t e;
   const bool low_precision = cfg->expert_dtype == MOE_DTYPE_FP4_E2M1 ||
                              cfg->expert_dtype == MOE_DTYPE_FP8_E4M3_B128;
+  // Once the side stream is forked, every return joins it back into s first
+  // (the join recorded again after whatever reached the side stream), so no
+  // side work is left unordered against the caller's next work on s, also
+  // when a launch fails.
+  hipStream_t s2 = nullptr;
+  SideEvents *side = nullptr;
+  auto finish = [&](int status) {
+    if (side) {
+      (void)hipEventRecord(side->join, s2);
+      (void)hipStreamWaitEvent(s, side->join, 0);
+    }
+    return status;
+  };
   if (side_stream && cfg->act_dtype == MOE_DTYPE_BF16 && low_precision &&
       (p.has_shared || p.mx)) {
-    hipStream_t s2 = (hipStream_t)side_stream;
-    SideEvents *side = nullptr;
-    if (side_events(&side) != hipSuccess) return MOE_ERR_HIP;
-    if (hipEventRecord(side->fork, s) != hipSuccess ||
-        hipStreamWaitEvent(s2, side->fork, 0) != hipSuccess)
-      return MOE_ERR_HIP;
+    s2 = (hipStream_t)side_stream;
+    SideEvents *ev = nullptr;
+    if (side_events(&ev) != hipSuccess) return MOE_ERR_HIP;
+    if (hipEventRecord(ev->fork, s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamWaitEvent(s2, ev->fork, 0) != hipSuccess) return MOE_ERR_HIP;
+    side = ev;
     if (moe::launch_shared_expert(p, s2, side->xq_ready) != hipSuccess ||
         hipEventRecord(side->join, s2) != hipSuccess)
-      return MOE_ERR_HIP;
+      return finish(MOE_ERR_HIP);
     p.shared_done = side->join;
     p.xq_ready = p.mx ? side->xq_ready : nullptr;
   }
 
-  if (events && hipEventRecord(events[MOE_STAGE_ROUTE], s) != hipSuccess) return MOE_ERR_HIP;
+  if (events && hipEventRecord(events[MOE_STAGE_ROUTE], s) != hipSuccess)
+    return finish(MOE_ERR_HIP);
   if (hash) {
-    if ((e = moe::launch_clear_flags(flags, s)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = moe::launch_clear_flags(flags, s)) != hipSuccess) return finish(MOE_ERR_HIP);
     if (cfg->route_mode == MOE_ROUTE_NGRAM_HASH) {
       int64_t q[16];
       primes_above(cfg->vocab_size, k, q);
@@ -466,7 +521,7 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
     e = moe::launch_route_learned(*cfg, x, w->gate_w, w->gate_bias, T, route_w, route_idx, s,
                                   moe::route_logits_floats(*cfg, T) ? logits : nullptr);
   }
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (e != hipSuccess) return finish(MOE_ERR_HIP);
 
   moe::TileSpec ts;
   ts.tiles = tiles;
@@ -476,11 +531,13 @@ static int forward_impl(const moe_config *cfg, const moe_weights *w, const void 
   ts.shared_rows_tok = sorted_tok + T * k;
   ts.route_w = route_w;
   ts.sorted_w = sorted_w;
-  if (events && hipEventRecord(events[MOE_STAGE_PERMUTE], s) != hipSuccess) return MOE_ERR_HIP;
+  if (events && hipEventRecord(events[MOE_STAGE_PERMUTE], s) != hipSuccess)
+    return finish(MOE_ERR_HIP);
   e = moe::launch_permute(cfg->n_routed_experts, k, T, route_idx, counts, offsets, sorted_tok,
                           sorted_slot, inverse, flags, &ts, /*clear_flags=*/!hash, s, perm_hist);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_experts(p, s));
+  if (e != hipSuccess) return finish(MOE_ERR_HIP);
+  if (moe::launch_experts(p, s) != hipSuccess) return finish(MOE_ERR_HIP);
+  return MOE_OK;
 }
 
 int moe_pack_weights(const moe_config *cfg, const moe_weights *src, const moe_weights *dst,

@@ -298,3 +298,23 @@ def test_forward_ex_argument_checks():
     # T == 0 is a no-op that returns before any stream is touched
     assert f(ctypes.byref(cfg_c), ctypes.byref(w), fake, None, 0, fake, fake, 0, None,
              s, ctypes.c_void_p(0x3000)) == B.MOE_OK
+
+
+def test_forward_ex_side_stream_error_returns_status():
+    """With a side stream on a host where the HIP runtime has no usable
+    device, moe_forward_ex passes every host check and then reports
+    MOE_ERR_HIP from the side-stream set-up (event creation needs a device)
+    instead of crashing; nothing is launched.  Skipped where a device exists."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: the no-device path cannot be reached")
+    cfg = C.V41_FLASH_FP4_MX.cfg
+    cfg_c = B.config_c(cfg)
+    fake = ctypes.c_void_p(0x100000)
+    w = B.MoeWeightsC(*([fake] * 12))
+    T = 64
+    need = B.moe_workspace_size(cfg, T)
+    st = B._lib.moe_forward_ex(ctypes.byref(cfg_c), ctypes.byref(w), fake, None, T,
+                               ctypes.c_void_p(0x200000), fake, need, None,
+                               ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000))
+    assert st == B.MOE_ERR_HIP

@@ -66,12 +66,12 @@ def test_pack_layout(name, gpu):
     assert packed["gate_w"] is layer["gate_w"]
 
 
-def _forward(cfg, layer, T, device):
+def _forward(cfg, layer, T, device, with_ws=False):
     ws = B.alloc_workspace(cfg, T, device)
     y = torch.empty_like(layer["x"])
     B.moe_forward(cfg, layer, layer["x"], layer["token_ids"], T, y, ws)
     torch.cuda.synchronize()
-    return y
+    return (y, ws) if with_ws else y
 
 
 @pytest.mark.parametrize("name", [n for n, w in C.SMALL_WORKLOADS.items()
@@ -103,11 +103,13 @@ def test_forward_tiled_decode_and_single_token(gpu):
         sub = dict(layer, x=layer["x"][:T].contiguous())
         psub = dict(packed, x=sub["x"])
         y_rows = _forward(cfg, sub, T, gpu)
-        y_tiled = _forward(tcfg, psub, T, gpu)
+        y_tiled, ws = _forward(tcfg, psub, T, gpu, with_ws=True)
         assert torch.equal(y_rows.view(torch.int16), y_tiled.view(torch.int16))
+        v = B.workspace_views(cfg, T, ws)
         ow, oidx, aux = H.oracle_route(cfg, sub)
-        keep = ~H.near_tie_tokens(cfg, aux) if aux is not None else np.ones(T, bool)
-        yref = oracle.layer_forward(H.f64(sub["x"])[keep], ow[keep], oidx[keep],
+        rc = H.check_routing(cfg, H.cpu_np(v["route_weights"]), H.cpu_np(v["route_indices"]),
+                             ow, oidx, aux, label=f"decode T={T}")
+        yref = oracle.layer_forward(H.f64(sub["x"]), rc.ref_w, rc.idx,
                                     H.expert_fetcher(layer, cfg), H.shared_weights(layer, cfg),
                                     cfg.swiglu_limit)
-        assert H.max_rel_err(H.f64(y_tiled)[keep], yref) <= H.TOL["bf16"]
+        H.check_layer_output(cfg, H.f64(y_tiled), yref, label=f"decode T={T}")
