@@ -318,8 +318,14 @@ size_t moe_workspace_size(const moe_config *cfg, int64_t T); /* 0 if invalid */
  *             Ids outside [0, vocab_size) route like token 0 (2-gram: like
  *             the pair (vocab_size, 0)) with weight 0 and set
  *             MOE_FLAG_TOKEN_ID_RANGE in the forward's flags
- * The score GEMM, affinity, bias, group limit, top-k and renormalisation run
- * in one kernel; logits never leave the chip. */
+ * Learned routing runs in one kernel: a workgroup owns 32 tokens and all E
+ * experts, the score GEMM (bf16 MFMA, fp32 accumulation; fp32 FMAs for fp32
+ * layers) leaves the logits in LDS, and the affinity, bias, group limit,
+ * top-k and renormalisation run there; only weights and indices are written.
+ * moe_forward, which has a workspace, routes with a split form instead (the
+ * score GEMM split over the input dimension, its fp32 partial logits added
+ * in order by the selection kernel): measured faster at every batch size,
+ * see moe_forward.  Both forms select identically. */
 int moe_route(const moe_config *cfg, const moe_weights *w, const void *x,
               const int32_t *token_ids, int64_t T,
               float *weights, int32_t *indices, void *stream);
@@ -347,6 +353,14 @@ int moe_permute(const moe_config *cfg, const int32_t *indices, int64_t T,
  *   ws  device workspace of at least moe_workspace_size(cfg, T) bytes,
  *       256-byte aligned; its sub-buffers (moe_ws_layout) hold the
  *       routing, permutation and intermediates of this call afterwards.
+ * Learned bf16 routing inside the forward uses the split score GEMM: kp
+ * partial [T, E] fp32 logit slices go to the workspace (route_logits) and the
+ * selection kernel adds them in order.  That costs a round trip of
+ * kp * T * E * 4 bytes (V3 prefill, T = 4096, E = 256, kp = 8: 33.6 MB each
+ * way), but spreads the gate-weight stream over many workgroups: the route
+ * stage takes 48 us there against 99 us for moe_route's one-kernel form
+ * (23 against 90 us at T = 64), whose workgroups must each stream the whole
+ * gate matrix.
  * Everything is enqueued on `stream`; nothing persists between calls.  The
  * call enqueues only kernels (and, in the variants below, event records and
  * waits): no host synchronisation, allocation or memset.  So it can be

@@ -17,6 +17,7 @@
 #include <climits>
 
 #include "common.h"
+#include "gemm.h"
 #include "internal.h"
 
 namespace moe {
@@ -164,95 +165,146 @@ __device__ __forceinline__ void select_token(const RouteArgs &a, const float *zr
 }
 
 // ---------------------------------------------------------------------------
-// bf16 layers: logits on MFMA.  MT 16-token row blocks per workgroup; the E
-// experts are cut into 16-wide column blocks, wave group member c (of 4)
-// owning blocks c, c+4, ... (EPL = ceil(E/64) of them, the same count as
-// experts per lane in phase 2).  KS wave groups split the input dimension;
-// their partial logits are added in LDS in a fixed order.  Each wave keeps
-// NSR k-steps of operands in flight in a register ring; every load is
-// unconditional (rows past T or E re-read a valid row and their logits are
-// dropped), so the compiler's waits stay static.
-template <int EPL, int MT, int KS>
-__global__ __launch_bounds__(256 * KS) void route_learned_bf16(const RouteArgs a) {
-  constexpr int BT = 16 * MT, NSR = 4;
-  extern __shared__ float zl[];                 // [BT][E + 1]
+// bf16 layers, fused: one workgroup (4 waves) owns 32 tokens and all E
+// experts, so every logit of a token ends up in the workgroup's LDS and the
+// selection runs on it there; only the k (index, weight) pairs per token
+// reach HBM.
+//
+// Score GEMM z = x Wg^T on v_mfma_f32_32x32x16_bf16 (operand layout as in
+// dense.hip: lane l, r = l % 32, h = l / 32 holds row / column r, inputs
+// 8h .. 8h+7 of a 16-input step; the accumulator holds column r, rows
+// 8(i/4) + 4h + i%4).  The input dimension runs in 64-input stages through
+// an NS-deep LDS copy ring: per stage the 32 token rows (4 units) and the
+// E_pad = 128 CPW gate rows (16 CPW units), each unit 8 rows x 128 bytes,
+// copied global -> LDS by the DMA form of the 16-byte load (lane l takes row
+// l/8, chunk (l%8) ^ (l/8), so every copied row is one full cache line and
+// each 8-lane read phase hits distinct banks).  Wave w owns the CPW 32-expert
+// column blocks w*CPW ..; every wave reads the shared token block.  Gate rows
+// past E re-read row E-1 and token rows past T row T-1; their logits are
+// dropped.  The ring slots are separate LDS objects and the steady-state
+// loop has no branch, so the compiler adds no waits between a copy into one
+// slot and a read of another; the waits are the explicit vmcnt counts.
+//
+// After the last stage the logits go to LDS ([32][E + 1] fp32, over the
+// ring) and each wave runs select_token on 8 of the tokens.
+template <int CPW, int NS>
+constexpr int route_fused_slot_bytes() { return (4 + 16 * CPW) * 1024; }
+
+template <int EPL, int CPW, int NS>
+__global__ __launch_bounds__(256) void route_fused_bf16(const RouteArgs a) {
+  constexpr int BT = 32;
+  constexpr int XU = 4;                        // token units per stage
+  constexpr int UNITS = XU + 16 * CPW;
+  constexpr int VM = UNITS / 4;                // copies per wave and stage
+  constexpr int SLOT = route_fused_slot_bytes<CPW, NS>();
+  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * VM <= 63, "ring depth");
+  static_assert(SLOT >= BT * (64 * EPL + 1) * 4, "logit tile fits the first ring slot");
+  __shared__ __attribute__((aligned(1024))) uint8_t S0[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t S1[SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t S2[NS > 2 ? SLOT : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t S3[NS > 3 ? SLOT : 1];
+  uint8_t *const ring[4] = {S0, S1, S2, S3};
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wc = wave & 3, ks = wave >> 2;
   const int64_t t0 = (int64_t)blockIdx.x * BT;
-  const int E = a.E, d = a.d, ldz = E + 1;
-  const int dk = d / KS;                        // d % 64 == 0, so dk % 32 == 0
-  const int nsteps = dk / 32;
+  const int E = a.E, d = a.d;
   const bf16 *x = (const bf16 *)a.x;
   const bf16 *w = (const bf16 *)a.w;
 
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const bf16 *xrow[MT];
+  // copy sources: unit u = wave + 4q; units 0..3 are token rows, the rest
+  // gate rows 8(u - 4) ..
+  const uint8_t *src[VM];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int64_t t = t0 + m * 16 + r16;
-    xrow[m] = x + (t < a.T ? t : a.T - 1) * (int64_t)d + ks * dk + kq;
+  for (int q = 0; q < VM; ++q) {
+    const int u = wave + 4 * q;
+    const int chunk = (lane & 7) ^ (lane >> 3);
+    if (u < XU) {
+      int64_t t = t0 + u * 8 + (lane >> 3);
+      t = t < a.T ? t : a.T - 1;
+      src[q] = (const uint8_t *)(x + t * d) + 16 * chunk;
+    } else {
+      int e = (u - XU) * 8 + (lane >> 3);
+      e = e < E ? e : E - 1;
+      src[q] = (const uint8_t *)(w + (int64_t)e * d) + 16 * chunk;
+    }
   }
-  const bf16 *wrow[EPL];
+  const int r32 = lane & 31, h = lane >> 5, rr = lane & 7;
+  int off[4];
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = (wc + 4 * j) * 16 + r16;
-    wrow[j] = w + (int64_t)(e < E ? e : E - 1) * d + ks * dk + kq;
-  }
-  f32x4 acc[MT][EPL];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < 4; ++s) off[s] = (r32 >> 3) * 1024 + (rr * 8 + ((2 * s + h) ^ rr)) * 16;
 
-  bf16x8 an[NSR][MT], bn[NSR][EPL];
-  auto load = [&](int slot, int step) {
-    const int off = step * 32;
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  f32x16 acc[CPW];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) an[slot][m] = *(const bf16x8 *)(xrow[m] + off);
+  for (int j = 0; j < CPW; ++j)
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) bn[slot][j] = *(const bf16x8 *)(wrow[j] + off);
+    for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+
+  const int nst = d / 64;
+  const int last = nst - 1;
+  auto issue = [&](int SL, int ST, int q) {
+    dma16(src[q] + (int64_t)ST * 128, ring[SL] + (wave + 4 * q) * 1024);
   };
-  const int last = nsteps - 1;
 #pragma unroll
-  for (int p = 0; p < NSR - 1; ++p) load(p, p < last ? p : last);
-  for (int s0 = 0; s0 < nsteps; s0 += NSR) {
+  for (int p = 0; p < NS - 1; ++p)
 #pragma unroll
-    for (int p = 0; p < NSR; ++p) {
+    for (int q = 0; q < VM; ++q) issue(p, p < last ? p : last, q);
+
+  auto compute_stage = [&](int p, int nx) {
+    const int nslot = (p + NS - 1) % NS;
+    const uint8_t *base = ring[p];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 av = *(const bf16x8 *)(base + off[s]);
+      bf16x8 bv[CPW];
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+        bv[j] = *(const bf16x8 *)(base + (XU + 4 * (wave * CPW + j)) * 1024 + off[s]);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[j], acc[j], 0, 0, 0);
+      // this k-step's share of the refill of the slot the previous stage used
+#pragma unroll
+      for (int q = s * ((VM + 3) / 4); q < (s + 1) * ((VM + 3) / 4) && q < VM; ++q)
+        issue(nslot, nx, q);
+    }
+  };
+
+  const int nfull = nst - nst % NS;
+  for (int s0 = 0; s0 < nfull; s0 += NS) {
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
       const int st = s0 + p;
-      const int nx = st + NSR - 1;
-      load((p + NSR - 1) % NSR, nx < last ? nx : last);
-      if (st < nsteps) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int j = 0; j < EPL; ++j)
-            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(an[p][m], bn[p][j], acc[m][j],
-                                                                0, 0, 0);
-      }
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT((NS - 2) * VM));
+      __builtin_amdgcn_s_barrier();
+      compute_stage(p, st + NS - 1 < last ? st + NS - 1 : last);
     }
   }
-  // logits -> LDS: lane holds expert column r16 of each block, rows
-  // 4*(lane>>4)+i; the K parts are summed in order ks = 0, 1, ...
 #pragma unroll
-  for (int part = 0; part < KS; ++part) {
-    if (ks == part) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-          const int e = (wc + 4 * j) * 16 + r16;
-          if (e < E) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float *z = zl + (m * 16 + (lane >> 4) * 4 + i) * ldz + e;
-              *z = part == 0 ? acc[m][j][i] : *z + acc[m][j][i];
-            }
-          }
-        }
+  for (int p = 0; p < NS - 1; ++p) {
+    const int st = nfull + p;
+    if (st < nst) {
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+      __builtin_amdgcn_s_barrier();
+      compute_stage(p, st + NS - 1 < last ? st + NS - 1 : last);
     }
-    __syncthreads();
   }
-  for (int tl = wave; tl < BT; tl += 4 * KS) {
+  __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+  __syncthreads();                             // every wave is done with the ring
+
+  // logits -> LDS [token][expert], over the first ring slot
+  float *zl = (float *)S0;
+  const int ldz = E + 1;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int e = 32 * (wave * CPW + j) + r32;
+    if (e < E) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zl[(8 * (i >> 2) + 4 * h + (i & 3)) * ldz + e] = acc[j][i];
+    }
+  }
+  __syncthreads();
+  for (int tl = wave; tl < BT; tl += 4) {
     const int64_t t = t0 + tl;
     if (t < a.T) select_token<EPL>(a, zl + tl * ldz, t, lane);
   }
@@ -505,28 +557,25 @@ hipError_t launch_update_bias(const int32_t *counts, int E, int64_t T, int k, fl
 }
 
 // ---------------------------------------------------------------------------
+// The fused bf16 router's configuration for E experts: CPW = ceil(E / 128)
+// 32-expert blocks per wave; a 3-stage ring where it fits the 160 KB of LDS
+// (E <= 384), else 2 stages.
+template <int EPL>
+static hipError_t launch_fused_epl(const RouteArgs &a, hipStream_t s) {
+  constexpr int CPW = (EPL + 1) / 2;
+  constexpr int NS = CPW <= 3 ? 3 : 2;
+  static_assert(NS * route_fused_slot_bytes<CPW, NS>() <= 160 * 1024, "LDS");
+  const dim3 grid((unsigned)((a.T + 31) / 32));
+  hipLaunchKernelGGL((route_fused_bf16<EPL, CPW, NS>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int EPL>
 static hipError_t launch_learned_epl(const RouteArgs &a, int act_dtype, hipStream_t s) {
-  if (act_dtype == MOE_DTYPE_BF16) {
-    // one 16-token block per workgroup until that gives more workgroups than
-    // CUs, then two (halves the gate-weight re-reads from L2)
-    const int MT = a.T > 4096 ? 2 : 1;
-    const int BT = 16 * MT;
-    const size_t lds = (size_t)BT * (a.E + 1) * sizeof(float);
-    const dim3 grid((unsigned)((a.T + BT - 1) / BT));
-    if (MT == 2) {
-      if (lds > 65536)
-        (void)hipFuncSetAttribute((const void *)route_learned_bf16<EPL, 2, 2>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      hipLaunchKernelGGL((route_learned_bf16<EPL, 2, 2>), grid, dim3(512), lds, s, a);
-    } else {
-      hipLaunchKernelGGL((route_learned_bf16<EPL, 1, 2>), grid, dim3(512), lds, s, a);
-    }
-  } else {
-    const size_t lds = (size_t)16 * (a.E + 1) * sizeof(float);
-    const dim3 grid((unsigned)((a.T + 15) / 16));
-    hipLaunchKernelGGL((route_learned_f32<EPL>), grid, dim3(256), lds, s, a);
-  }
+  if (act_dtype == MOE_DTYPE_BF16) return launch_fused_epl<EPL>(a, s);
+  const size_t lds = (size_t)16 * (a.E + 1) * sizeof(float);
+  const dim3 grid((unsigned)((a.T + 15) / 16));
+  hipLaunchKernelGGL((route_learned_f32<EPL>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
