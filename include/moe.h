@@ -371,6 +371,27 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                 const int32_t *token_ids, int64_t T, void *y,
                 void *ws, size_t ws_bytes, void *stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the workspace is a fixed device array inside the library, one per GPU,
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) large and held until the process ends.
+ * The caller still passes the inputs, the weights and y; arguments and
+ * results are as moe_forward's.
+ *   Returns MOE_ERR_WORKSPACE, before any launch, when moe_workspace_size(cfg,
+ *   T) exceeds MOE_NOALLOC_SCRATCH_BYTES (V3 / V4.1-Flash shapes: decode
+ *   batches of up to a few hundred tokens fit; large prefill batches do not),
+ *   MOE_ERR_HIP if the array's device address cannot be obtained.
+ * The call allocates nothing: the array's device address is taken once per
+ * GPU (hipGetSymbolAddress, on the first call there).  Nothing in it needs to
+ * start at zero (the kernels clear their flag words themselves).  Every call
+ * on one GPU uses the same array and it keeps the last call's contents:
+ * calls that overlap on one GPU (two streams, or two host threads without
+ * ordering) race on it, so the caller orders them.  The workspace views of
+ * moe_ws_layout are not exposed for this entry point. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, const void *x,
+                        const int32_t *token_ids, int64_t T, void *y, void *stream);
+
 /* Stages of moe_forward in launch order (for moe_forward_profiled). */
 #define MOE_STAGE_ROUTE 0     /* router kernel (or hash gather)                  */
 #define MOE_STAGE_PERMUTE 1   /* permute kernel                                 */

@@ -25,12 +25,13 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 MOE_FLAG_TOKEN_ID_RANGE = 1
 MOE_FLAG_EXPERT_RANGE = 2
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout",
     "moe_workspace_size", "moe_route", "moe_permute", "moe_forward", "moe_forward_profiled",
     "moe_pack_weights", "moe_build_tid2eid_multistart", "moe_update_bias", "moe_probe_read",
-    "moe_probe_mfma", "moe_redequant_fp8", "moe_forward_ex",
+    "moe_probe_mfma", "moe_redequant_fp8", "moe_forward_ex", "moe_forward_noalloc",
 )
 MOE_STAGES = ("route", "permute", "gemm1", "gemm2", "combine")
 
@@ -89,8 +90,10 @@ def _load():
                                          ctypes.POINTER(ctypes.c_void_p), vp]
     lib.moe_forward_ex.argtypes = [cfgp, wp, vp, vp, i64, vp, vp, ctypes.c_size_t,
                                    ctypes.POINTER(ctypes.c_void_p), vp, vp]
+    lib.moe_forward_noalloc.argtypes = [cfgp, wp, vp, vp, i64, vp, vp]
     for f in ("moe_validate_config", "moe_build_tid2eid", "moe_workspace_layout", "moe_route",
               "moe_permute", "moe_forward", "moe_forward_profiled", "moe_forward_ex",
+              "moe_forward_noalloc",
               "moe_pack_weights",
               "moe_build_tid2eid_multistart", "moe_update_bias", "moe_probe_read",
               "moe_probe_mfma"):
@@ -311,6 +314,13 @@ def moe_forward_ex(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, ws, eve
                                _ptr(x), _ptr(token_ids), T, _ptr(y), _ptr(ws),
                                ws.numel() * ws.element_size(), arr, _stream(stream), side),
            "moe_forward_ex")
+
+
+def moe_forward_noalloc(cfg: MoEConfig, layer: dict, x, token_ids, T: int, y, stream=None):
+    """moe_forward on the library's own device array (no workspace argument)."""
+    _check(_lib.moe_forward_noalloc(ctypes.byref(config_c(cfg)), ctypes.byref(weights_c(layer)),
+                                    _ptr(x), _ptr(token_ids), T, _ptr(y), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 class HipEvents:

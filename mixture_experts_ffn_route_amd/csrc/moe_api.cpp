@@ -241,6 +241,35 @@ void greedy_in_order(const double *p, const int64_t *order, int64_t m, int32_t n
   }
 }
 
+// Device memory of moe_forward_noalloc: one array per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: its address on each device comes from hipGetSymbolAddress,
+// taken once per device (with that device current) on the first call there,
+// and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex &scratch_mutex() {
+  static std::mutex *m = new std::mutex;
+  return *m;
+}
+
+hipError_t scratch_address(void **out) {
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex());
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 void max_min(const std::vector<double> &f, double *mx, double *mn) {
   *mx = f[0];
   *mn = f[0];
@@ -589,6 +618,19 @@ int moe_forward(const moe_config *cfg, const moe_weights *w, const void *x,
                 const int32_t *token_ids, int64_t T, void *y, void *ws, size_t ws_bytes,
                 void *stream) {
   return forward_impl(cfg, w, x, token_ids, T, y, ws, ws_bytes, nullptr, stream, nullptr);
+}
+
+int moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, const void *x,
+                        const int32_t *token_ids, int64_t T, void *y, void *stream) {
+  moe_ws_layout L;
+  const int st = make_layout(cfg, T, &L);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (L.total_bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return forward_impl(cfg, w, x, token_ids, T, y, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, nullptr,
+                      stream, nullptr);
 }
 
 int moe_forward_profiled(const moe_config *cfg, const moe_weights *w, const void *x,
