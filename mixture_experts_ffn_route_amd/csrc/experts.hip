@@ -69,7 +69,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
   // FP4 one 8-byte load (16 codes) plus one scale byte
   constexpr int NBV = NB * NCB * (FP4 ? 2 : NQ);
   constexpr int VM_PER_STAGE = NFW + NBV;          // every wave issues exactly this many
-  constexpr int CH = MBE < MCH ? MBE : MCH;
+  constexpr int CH = MBE < MCH ? MBE : (MBE % MCH == 0 ? MCH : 2);
   static_assert(NS >= 2, "pipeline needs two stages");
   static_assert((NS - 2) * VM_PER_STAGE <= 63, "vmcnt holds 6 bits");
   static_assert(NFW * WAVES * FRAG <= SLOT, "ring slot too small");
@@ -337,13 +337,19 @@ void grouped_gemm(const GemmArgs g) {
   if constexpr (MB < MCH) {
     gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT>(g, t, As);
   } else {
-    const int nch = (nmb + MCH - 1) / MCH;
-    if (nch <= 1 || MB < 2 * MCH)
-      gemm_tile<WAVES, NB, NCB, (MB < MCH ? MB : MCH), FP4, NS, SLOT>(g, t, As);
-    else if (nch == 2 || MB < 3 * MCH)
-      gemm_tile<WAVES, NB, NCB, (MB < 2 * MCH ? MB : 2 * MCH), FP4, NS, SLOT>(g, t, As);
-    else if (nch == 3 || MB < 4 * MCH)
-      gemm_tile<WAVES, NB, NCB, (MB < 3 * MCH ? MB : 3 * MCH), FP4, NS, SLOT>(g, t, As);
+    const int n2 = (nmb + 1) / 2 * 2;
+    if (n2 <= 4 || MB <= 4)
+      gemm_tile<WAVES, NB, NCB, (MB < 4 ? MB : 4), FP4, NS, SLOT>(g, t, As);
+    else if (n2 <= 6 || MB <= 6)
+      gemm_tile<WAVES, NB, NCB, (MB < 6 ? MB : 6), FP4, NS, SLOT>(g, t, As);
+    else if (n2 <= 8 || MB <= 8)
+      gemm_tile<WAVES, NB, NCB, (MB < 8 ? MB : 8), FP4, NS, SLOT>(g, t, As);
+    else if (n2 <= 10 || MB <= 10)
+      gemm_tile<WAVES, NB, NCB, (MB < 10 ? MB : 10), FP4, NS, SLOT>(g, t, As);
+    else if (n2 <= 12 || MB <= 12)
+      gemm_tile<WAVES, NB, NCB, (MB < 12 ? MB : 12), FP4, NS, SLOT>(g, t, As);
+    else if (n2 <= 14 || MB <= 14)
+      gemm_tile<WAVES, NB, NCB, (MB < 14 ? MB : 14), FP4, NS, SLOT>(g, t, As);
     else
       gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT>(g, t, As);
   }

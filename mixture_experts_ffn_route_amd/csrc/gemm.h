@@ -51,10 +51,13 @@ __device__ __forceinline__ void dma16(const void *gsrc, void *lds_block) {
 // i.e. not waited on).
 #define MOE_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-// Row blocks are processed in chunks of MCH (a tile's block count is rounded
-// up to a multiple of MCH): every pipeline stage is then straight-line code
+// Row blocks are processed in chunks of MCH (2 where MCH does not divide the
+// tile body's block count): every pipeline stage is then straight-line code
 // in which the LDS reads of a chunk issue back to back and the MFMAs of one
-// chunk overlap the reads of the next.  Padding blocks read real rows (the
+// chunk overlap the reads of the next.  A tile runs the body for its block
+// count rounded up to an even number (bodies of 4, 6, 8, ... blocks: measured
+// 3-6 % faster on the FP4 and hash layers than multiples of 4, whose padding
+// blocks cost MFMA issue slots there).  Padding blocks read real rows (the
 // tile's last row) and are never stored.
 constexpr int MCH = 4;
 
