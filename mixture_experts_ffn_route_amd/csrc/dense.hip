@@ -155,6 +155,9 @@ __device__ __forceinline__ void dense_tile(const DenseArgs &g, int64_t m0, int n
 #pragma unroll
       for (int q = s * ((VM + 3) / 4); q < (s + 1) * ((VM + 3) / 4) && q < VM; ++q)
         issue(nslot, nx, q);
+      // keep them here: the scheduler otherwise sinks every copy below the
+      // stage's MFMAs, a stage less of prefetch
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 

@@ -203,69 +203,89 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p) issue_stage(p, p < last ? p : last);
 
-  // Every iteration issues exactly one stage of loads per step, so the number
-  // of vector memory ops between a stage's issue and its use is the constant
-  // (NS-1) * VM_PER_STAGE and every wait below is a compile-time vmcnt.
-  for (int s0 = 0; s0 < nst; s0 += NS) {
+  // One pipeline stage: stage st from ring slot p; refills the slot freed by
+  // stage st-1 with stage st+NS-1 (clamped to the last stage), spread over
+  // the MFMA chunks, so a load that waits for queue space stalls the wave
+  // while issued MFMAs keep the matrix unit busy.  A scheduling barrier after
+  // each chunk keeps the loads there: the scheduler otherwise sinks them
+  // below the stage's MFMAs (shorter live ranges), a stage less of prefetch.
+  // (All refills right after the barrier measured slower: hash GEMM1
+  // 0.20 -> 0.35 ms, FP4 GEMM1 1.96 -> 2.10 ms.)
+  auto compute_stage = [&](int p, int st) {
+    const int nslot = (p + NS - 1) % NS;
+    const int nx = st + NS - 1 < last ? st + NS - 1 : last;
+    const bf16 *abase = As + p * SLOT;
 #pragma unroll
-    for (int p = 0; p < NS; ++p) {
-      const int st = s0 + p;
-      // stages st+1 .. st+NS-2 may stay in flight
-      __builtin_amdgcn_s_waitcnt(MOE_VMCNT((NS - 2) * VM_PER_STAGE));
-      __builtin_amdgcn_s_barrier();     // every wave's copies for st landed; st-1 fully read
-      // the refill of the slot freed by stage st-1 (stage st+NS-1) is spread
-      // over this stage's MFMA chunks, so a load that waits for queue space
-      // stalls the wave while issued MFMAs keep the matrix unit busy
-      const int nslot = (p + NS - 1) % NS;
-      const int nx = st + NS - 1 < last ? st + NS - 1 : last;
-      if (st >= nst) issue_stage(nslot, nx);
-      if (st < nst) {
-        const bf16 *abase = As + p * SLOT;
+    for (int sub = 0; sub < SUBS; ++sub) {
+      bf16x8 bf[NB][NCB];
 #pragma unroll
-        for (int sub = 0; sub < SUBS; ++sub) {
-          bf16x8 bf[NB][NCB];
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          if constexpr (FP4) {
+            const unsigned word = sub == 0 ? fq[p][b][cb].x : fq[p][b][cb].y;
+            const float scale = __uint_as_float(sq[p][b][cb] << 23);
+            const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
+            const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
+            const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
+            const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
+            bf[b][cb] = bf16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+          } else {
+            bf[b][cb] = __builtin_bit_cast(bf16x8, bq[p][b][cb][sub]);
+          }
+        }
+#pragma unroll
+      for (int mc = 0; mc < MBE; mc += CH) {
+        bf16x8 a[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          a[j] = *(const bf16x8 *)(abase + aoff[sub] + (mc + j) * 2 * FRAG);
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
 #pragma unroll
           for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-              if constexpr (FP4) {
-                const unsigned word = sub == 0 ? fq[p][b][cb].x : fq[p][b][cb].y;
-                const float scale = __uint_as_float(sq[p][b][cb] << 23);
-                const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
-                const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
-                const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
-                const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
-                bf[b][cb] = bf16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-              } else {
-                bf[b][cb] = __builtin_bit_cast(bf16x8, bq[p][b][cb][sub]);
-              }
-            }
+            for (int cb = 0; cb < NCB; ++cb)
+              acc[mc + j][b][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  a[j], bf[b][cb], acc[mc + j][b][cb], 0, 0, 0);
+        const int chunk = sub * (MBE / CH) + mc / CH;
 #pragma unroll
-          for (int mc = 0; mc < MBE; mc += CH) {
-            bf16x8 a[CH];
-#pragma unroll
-            for (int j = 0; j < CH; ++j)
-              a[j] = *(const bf16x8 *)(abase + aoff[sub] + (mc + j) * 2 * FRAG);
-#pragma unroll
-            for (int j = 0; j < CH; ++j)
-#pragma unroll
-              for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                  acc[mc + j][b][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                      a[j], bf[b][cb], acc[mc + j][b][cb], 0, 0, 0);
-            const int chunk = sub * (MBE / CH) + mc / CH;
-#pragma unroll
-            for (int j = 0; j < ISSUE_PER_CHUNK; ++j) {
-              const int q = chunk * ISSUE_PER_CHUNK + j;
-              if (q < VM_PER_STAGE) issue_op(nslot, nx, q);
-            }
-          }
+        for (int j = 0; j < ISSUE_PER_CHUNK; ++j) {
+          const int q = chunk * ISSUE_PER_CHUNK + j;
+          if (q < VM_PER_STAGE) issue_op(nslot, nx, q);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+
+  // Whole groups of NS stages: no branch inside, and every stage issues
+  // exactly one stage of copies, so the number of vector memory ops between
+  // a stage's issue and its use is the constant (NS-1) * VM_PER_STAGE and
+  // every wait is a compile-time vmcnt.  The compiler also waits by itself
+  // for the loads whose registers an MFMA reads; it can count those exactly
+  // only when every path through the loop issues the same memory ops (a
+  // `st < nst` branch around the compute made it wait for all outstanding
+  // ops at the start of most stages, draining the ring).
+  const int nfull = nst - nst % NS;
+  for (int s0 = 0; s0 < nfull; s0 += NS) {
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+      // stages st+1 .. st+NS-2 may stay in flight
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT((NS - 2) * VM_PER_STAGE));
+      __builtin_amdgcn_s_barrier();     // every wave's copies for st landed; st-1 fully read
+      compute_stage(p, s0 + p);
+    }
   }
-#undef MOE_ISSUE
+  // the last nst % NS stages, with full waits
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) {
+    if (nfull + p < nst) {
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+      __builtin_amdgcn_s_barrier();
+      compute_stage(p, nfull + p);
+    }
+  }
   // drain the trailing copies before the workgroup's LDS can be reused
   __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
 
@@ -551,7 +571,7 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
       else { MOE_TRY(8, 2, 1, true, 3) }
       MOE_TRY(4, 2, 1, true, 3)
     } else {
-      if (decode) { MOE_TRY_DECODE(4, 2, 1, false, 4) }
+      if (decode) { MOE_TRY_DECODE(4, 2, 1, false, 3) }
       else if (mb >= 16) { MOE_TRY(8, 2, 1, false, 4) }
       else { MOE_TRY(8, 2, 1, false, 3) }
       MOE_TRY(4, 2, 1, false, 3)
@@ -562,7 +582,7 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
       else { MOE_TRY(8, 1, 2, true, 3) }
       MOE_TRY(4, 1, 1, true, 3)
     } else {
-      if (decode) { MOE_TRY_DECODE(4, 1, 2, false, 4) }
+      if (decode) { MOE_TRY_DECODE(4, 1, 2, false, 3) }
       else { MOE_TRY(8, 1, 2, false, 3) }
       MOE_TRY(4, 1, 1, false, 3)
     }
