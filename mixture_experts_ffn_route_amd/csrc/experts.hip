@@ -290,39 +290,74 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
   __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
 
   // ---- epilogue ----
-  if constexpr (NB == 2) {
-    const float L = g.limit;
+  // fp32 output (router logits on this kernel's dense form): direct stores
+  if (NB == 1 && g.Cf) {
 #pragma unroll
     for (int m = 0; m < MBE; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = m * 16 + jq * 4 + i;
-        if (row < rows) {
-          bf16 *crow = g.C + (int64_t)(row0 + row) * N + col0 + r16;
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-            crow[cb * 16] = (bf16)swiglu_pair(acc[m][0][cb][i], acc[m][1][cb][i], L);
-        }
-      }
-  } else {
-#pragma unroll
-    for (int m = 0; m < MBE; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m * 16 + jq * 4 + i;
-        // row / 64 = m / 4 for every lane; every lane takes part in the shuffle
-        const float w = __shfl(my_w[m >> 2], row & 63);
+        const float w = __shfl(my_w[m >> 2], row & 63);   // every lane takes part
         if (row < rows) {
           const int64_t o = (int64_t)(row0 + row) * N + col0 + r16;
-          if (g.Cf) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) g.Cf[o + cb * 16] = acc[m][0][cb][i] * w;
-          } else {
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) g.C[o + cb * 16] = (bf16)(acc[m][0][cb][i] * w);
-          }
+          for (int cb = 0; cb < NCB; ++cb) g.Cf[o + cb * 16] = acc[m][0][cb][i] * w;
         }
       }
+    return;
+  }
+  // bf16 output, staged through the (now idle) LDS ring: every wave writes its
+  // bf16 results into a row-major [rows][slab] tile, then the workgroup stores
+  // whole rows with 16-byte stores, full cache lines, instead of a 2-byte
+  // store per value in the accumulator layout (lane = one column of four
+  // rows: 32-byte row segments).  Measured 1-4 % faster per GEMM (V4.1-Flash
+  // FP4 layer 3.53 -> 3.42 ms, 2-gram hash layer 0.427 -> 0.409 ms).  Rows are
+  // staged in chunks of RC that fit the ring; a 16-byte pad per staged row
+  // spreads the four row groups of a write over distinct banks.
+  constexpr int SW = WAVES * NCB * 16;               // slab columns
+  constexpr int STRIDE = SW + 8;                     // bf16 per staged row
+  constexpr int RC0 = NS * SLOT / STRIDE / 16 * 16;
+  constexpr int RC = RC0 < MBE * 16 ? RC0 : MBE * 16;
+  constexpr int NCHUNK = (MBE * 16 + RC - 1) / RC;
+  constexpr int CPR = SW / 8;                        // 16-byte pieces per row
+  constexpr int NT = WAVES * 64;
+  constexpr int ITER = (RC * CPR + NT - 1) / NT;
+  static_assert(RC >= 16 && RC % 16 == 0, "ring holds at least one row block");
+  const int slab0 = col0 - wave * NCB * 16;
+  const float L = g.limit;
+  // every wave's copies have landed (each waited above) and every wave is
+  // done reading the ring
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NCHUNK; ++c) {
+#pragma unroll
+    for (int m = c * RC / 16; m < (c + 1) * RC / 16 && m < MBE; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m * 16 + jq * 4 + i;
+        bf16 *srow = As + (row - c * RC) * STRIDE + wave * NCB * 16 + r16;
+        if constexpr (NB == 2) {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            srow[cb * 16] = (bf16)swiglu_pair(acc[m][0][cb][i], acc[m][1][cb][i], L);
+        } else {
+          // row / 64 = m / 4 for every lane; every lane takes part in the shuffle
+          const float w = __shfl(my_w[m >> 2], row & 63);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) srow[cb * 16] = (bf16)(acc[m][0][cb][i] * w);
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int idx = it * NT + (int)threadIdx.x;
+      const int rl = idx / CPR, pc = idx - rl * CPR;
+      const int row = c * RC + rl;
+      if (idx < RC * CPR && row < rows)
+        *(u32x4 *)(g.C + (int64_t)(row0 + row) * N + slab0 + pc * 8) =
+            *(const u32x4 *)(As + rl * STRIDE + pc * 8);
+    }
+    if (c + 1 < NCHUNK) __syncthreads();
   }
 }
 
