@@ -198,6 +198,39 @@ def test_forward_hash_skewed_multi_tile(gpu):
     assert H.max_rel_err(H.f64(y), yref) <= H.TOL["bf16"]
 
 
+@pytest.mark.parametrize("tiled", [False, True])
+def test_forward_learned_skewed_multi_tile(tiled, gpu):
+    """Learned routing where a large selection bias on the k experts of group 0
+    makes every token pick them: each holds T rows over several GEMM tiles
+    (tall tiles and ragged last tiles of one expert), the other experts get
+    none, and the gate values stay the unbiased, renormalised scores."""
+    base = C.SMALL_WORKLOADS["v3_small"]
+    wl = C.Workload("v3_all_same", base.cfg, T=611, seed=7)
+    cfg, T = wl.cfg, wl.T
+    layer = synth.make_layer(wl, gpu)
+    k, per_group = cfg.n_activated_experts, cfg.n_routed_experts // cfg.n_expert_groups
+    assert k <= per_group
+    bias = torch.zeros(cfg.n_routed_experts, dtype=torch.float32)
+    bias[:k] = 10.0
+    layer["gate_bias"] = bias.to(gpu)
+    run_cfg, run_layer = B.pack_layer(cfg, layer) if tiled else (cfg, layer)
+    ws = B.alloc_workspace(run_cfg, T, gpu)
+    y = torch.empty_like(layer["x"])
+    print(f"[forward] {wl.name} T={T} tiled={tiled}", flush=True)
+    B.moe_forward(run_cfg, run_layer, layer["x"], None, T, y, ws)
+    torch.cuda.synchronize()
+    v = B.workspace_views(run_cfg, T, ws)
+    counts = H.cpu_np(v["counts"])
+    assert np.array_equal(counts[:k], np.full(k, T)) and counts[k:].sum() == 0
+    assert int(v["tile_count"][0]) > 2 * k
+    ow, oidx, aux = H.oracle_route(cfg, layer)
+    rc = H.check_routing(cfg, H.cpu_np(v["route_weights"]), H.cpu_np(v["route_indices"]),
+                         ow, oidx, aux, label=wl.name)
+    yref = H.oracle_forward(cfg, H.f64(layer["x"]), rc.ref_w, rc.idx, layer)
+    H.check_layer_output(cfg, H.f64(y), yref, label=wl.name)
+    assert int(v["flags"][0]) == 0
+
+
 def test_forward_hash_bad_token_id_flagged(gpu):
     wl = C.SMALL_WORKLOADS["hash_small"]
     cfg, T = wl.cfg, wl.T
