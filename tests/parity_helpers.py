@@ -198,8 +198,8 @@ def check_routing(cfg, gpu_w, gpu_idx, ora_w, ora_idx, aux, label=""):
     """GPU routing against the oracle's.
 
     Indices: equal to the oracle's for every token, except that learned
-    routing may differ where the pages leave the choice open at the 1e-6
-    relative band of the benchmark spec (oracle fp32 keys): the k-th / (k+1)-th
+    routing may differ where the pages leave the choice open, inside a 1e-6
+    relative tie band (on the oracle's fp32 keys): the k-th / (k+1)-th
     keys, the g-th / (g+1)-th group scores, or the slot order of two selected
     experts.  Every differing token is validated rather than skipped: k
     distinct ids in [0, E); all of them in a set of kept groups that the band
