@@ -42,9 +42,12 @@ namespace moe {
 // activations, so the LDS block already has the MFMA A-operand layout and the
 // readers take 16 consecutive bytes per lane without bank conflicts -- and
 // (b) its own weight columns as 16-byte loads into a register ring
-// (bf16 weights: nontemporal in decode-height tiles, whose weights nothing
-// re-reads: V3 decode GEMM1 2.15 -> 1.96 ms; taller tiles keep plain loads,
-// which measured faster there).  Stage st
+// (bf16 weights: nontemporal where no other work item reads the same weight
+// fragment -- V3 decode GEMM1 2.15 -> 1.96 ms, hash layer GEMM1 0.203 ->
+// 0.199 ms and GEMM2 0.124 -> 0.119 ms; taller tiles whose weights other
+// tiles stream too -- an expert cut into several tiles, the shared expert,
+// the dense form -- run a body of their own with plain loads, so that the
+// re-reads can still hit the caches).  Stage st
 // is consumed NS-1 stages after it was issued; one vmcnt wait and one barrier
 // per stage.
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -57,7 +60,7 @@ __device__ __forceinline__ uint2 fp4_stream_load(const uint8_t *p) {
   return uint2{v[0], v[1]};
 }
 
-template <int WAVES, int NB, int NCB, int MBE, bool FP4, int NS, int SLOT>
+template <int WAVES, int NB, int NCB, int MBE, bool FP4, int NS, int SLOT, bool SH = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, bf16 *As) {
   constexpr int BK = 64;                   // inputs per stage
   constexpr int SUBS = BK / 32;            // MFMA k-steps per stage
@@ -189,7 +192,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
     } else {
       const int r = q - NFW, bc = r / NQ, qq = r - bc * NQ, b = bc / NCB, cb = bc - b * NCB;
       const u32x4 *src = (const u32x4 *)(bptr[b][cb] + ST * bst + qq * qst);
-      bq[SL][b][cb][qq] = MBE == 1 ? __builtin_nontemporal_load(src) : *src;
+      bq[SL][b][cb][qq] = (MBE == 1 || !SH) ? __builtin_nontemporal_load(src) : *src;
     }
   };
   auto issue_stage = [&](int SL, int ST) {
@@ -391,6 +394,12 @@ void grouped_gemm(const GemmArgs g) {
 
   if constexpr (MB < MCH) {
     gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT>(g, t, As);
+  } else if (!FP4 && (t.shared || t.reread)) {
+    // tiles whose weights other tiles stream too (an expert of several tiles,
+    // the shared expert, the dense form): plain weight loads (see above);
+    // such tiles are full height but for the last, so one body of MB blocks
+    // serves them
+    gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT, true>(g, t, As);
   } else {
     const int n2 = (nmb + 1) / 2 * 2;
     if (n2 <= 4 || MB <= 4)

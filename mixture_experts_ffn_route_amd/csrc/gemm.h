@@ -64,6 +64,8 @@ constexpr int MCH = 4;
 struct TileCtx {
   int grp, row0, rows, col0, lane, wave, K, N;
   bool shared;
+  bool reread;               // other tiles stream the same weights (several tiles of
+                             // one expert, the shared expert, or the dense form)
 };
 
 // 4-byte form: lane l's 4 bytes land at lds_block + 4*l.
@@ -109,7 +111,9 @@ __device__ __forceinline__ TileCtx gemm_tile_ctx(const GemmArgs &g, int tile, in
     t.grp = g.tiles[4 * tile];
     t.row0 = g.tiles[4 * tile + 1];
     t.rows = g.tiles[4 * tile + 2];
+    t.reread = g.tiles[4 * tile + 3] > 1;
   } else {
+    t.reread = true;
     t.grp = 0;
     t.row0 = tile * g.dense_tile_rows;
     const int64_t left = g.dense_rows - t.row0;

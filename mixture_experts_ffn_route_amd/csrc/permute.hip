@@ -8,7 +8,8 @@
 //   1. each wave histograms a contiguous chunk of pairs into its own LDS row;
 //   2. a scan over waves (per expert) and over experts gives every wave the
 //      first output row of each expert inside its chunk, plus counts/offsets
-//      and the GEMM work list (one tile per tile_rows rows of an expert);
+//      and the GEMM work list (one tile per tile_rows rows of an expert:
+//      expert, first row, rows, the expert's tile count);
 //   3. each wave walks its chunk 64 pairs at a time; lanes that hold the same
 //      expert find each other with one ballot per expert-id bit, take
 //      consecutive rows in lane order, and the last of them advances the
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const PermuteArgs
           td[0] = e;
           td[1] = off + r0;
           td[2] = (total - r0) < a.tile_rows ? (total - r0) : a.tile_rows;
-          td[3] = 0;
+          td[3] = ntile;                 // tiles of this expert
         }
       }
     }
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const PermuteArgs
       td[0] = E;
       td[1] = (int)(a.n + r0);
       td[2] = (a.T - r0) < a.tile_rows ? (int)(a.T - r0) : a.tile_rows;
-      td[3] = 0;
+      td[3] = a.n_shared_tiles;
     }
     for (int64_t t = tid; t < a.T; t += kPermThreads) a.shared_rows_tok[t] = (int32_t)t;
   }
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(const PermuteAr
           td[0] = e;
           td[1] = off + r0;
           td[2] = (total - r0) < a.tile_rows ? (total - r0) : a.tile_rows;
-          td[3] = 0;
+          td[3] = ntile;                 // tiles of this expert
         }
       }
     }
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(const PermuteAr
       td[0] = E;
       td[1] = (int)(a.n + r0);
       td[2] = (a.T - r0) < a.tile_rows ? (int)(a.T - r0) : a.tile_rows;
-      td[3] = 0;
+      td[3] = a.n_shared_tiles;
     }
     for (int64_t t = tid; t < a.T; t += kPermThreads) a.shared_rows_tok[t] = (int32_t)t;
   }
