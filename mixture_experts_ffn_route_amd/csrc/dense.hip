@@ -32,8 +32,6 @@
 namespace moe {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 struct DenseArgs {
   const bf16 *A;           // [M, K]
   int64_t M;

@@ -364,6 +364,238 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, const TileCtx &t, b
   }
 }
 
+// The same tile on v_mfma_f32_32x32x16_bf16 (bf16 weights), for tiles of two
+// or more row blocks.  One 32x32x16 instruction does the work of two
+// 16x16x32 ones, and a stream of them keeps the matrix pipe 99 % busy where
+// 16x16x32 reaches 57 % (MFMA-only probe, 8 waves per SIMD); each A operand
+// read from LDS also feeds twice the flops.  The grouped GEMMs are not bound
+// by the pipe, though: this form measured level with gemm_tile on most
+// shapes, and gemm_launch uses it only where it was faster.  Operand layout
+// (lane l, r = l % 32, h = l / 32): A row r, B column r, 8 inputs each
+// (which 8 of a k-step's 16 is free as long as A and B agree); D 16 floats,
+// column r, rows 8(e/4) + 4h + e%4 of the 32-row block.
+//
+// Here NCB counts 32-column blocks per wave and MBE 16-row blocks (even: the
+// MFMA takes 32-row blocks).  The activation copies are those of gemm_tile
+// (a 1 KB unit = 8 rows x 64 inputs, XOR-swizzled chunks); k-step s of a
+// stage reads 16-byte chunk 2s + h of the 64-input row.  Weights: per lane,
+// matrix, 32-column block and stage four 16-byte loads, k-step s from the
+// 16 x 32 tile (column block r / 16, inputs 32(s/2) ..) at tile lane
+// (r % 16) + 16(2(s%2) + h), i.e. inputs 16s + 8h .. of column r; the row
+// layout gives the same inputs.  Nontemporal unless other tiles stream the
+// same weights (SH), as in gemm_tile.
+template <int WAVES, int NB, int NCB, int MBE, int NS, int SLOT, int LDSE, bool SH = false>
+__device__ __forceinline__ void gemm_tile32(const GemmArgs &g, const TileCtx &t, bf16 *As) {
+  constexpr int BK = 64;                   // inputs per stage
+  constexpr int KS = BK / 16;              // MFMA k-steps per stage
+  constexpr int FRAG = 512;                // bf16 per 1 KB copy unit
+  static_assert(MBE % 2 == 0, "whole 32-row blocks");
+  constexpr int M32 = MBE / 2;
+  constexpr int NFRAG = MBE * 2;           // copy units per stage
+  constexpr int NFW = (NFRAG + WAVES - 1) / WAVES;
+  constexpr int NBV = NB * NCB * KS;       // weight loads per stage
+  constexpr int VM_PER_STAGE = NFW + NBV;
+  constexpr int CH = M32 % 4 == 0 ? 4 : (M32 % 2 == 0 ? 2 : 1);
+  constexpr int NCHK = KS * (M32 / CH);    // MFMA chunks per stage
+  constexpr int ISSUE_PER_CHUNK = (VM_PER_STAGE + NCHK - 1) / NCHK;
+  static_assert(NS >= 2, "pipeline needs two stages");
+  static_assert((NS - 2) * VM_PER_STAGE <= 63, "vmcnt holds 6 bits");
+  static_assert(NFW * WAVES * FRAG <= SLOT, "ring slot too small");
+
+  const int lane = t.lane, wave = t.wave, r32 = lane & 31, h = lane >> 5;
+  const int K = t.K, N = t.N, rows = t.rows, row0 = t.row0, col0 = t.col0;
+
+  constexpr int NWR = NB == 1 ? (16 * MBE + 63) / 64 : 1;
+  float my_w[NWR];
+#pragma unroll
+  for (int j = 0; j < NWR; ++j) {
+    const int r = 64 * j + lane;
+    const int64_t R = row0 + r;
+    my_w[j] = (NB == 1 && r < rows && R < g.routed_rows) ? g.sorted_w[R] : 1.f;
+  }
+
+  // activation copies: unit f = wave + WAVES*i holds rows 8f .. 8f+7
+  const bf16 *asrc[NFW];
+#pragma unroll
+  for (int i = 0; i < NFW; ++i) {
+    const int f0 = wave + WAVES * i;
+    const int f = f0 < NFRAG ? f0 : 0;
+    int r = 8 * f + (lane >> 3);
+    r = r < rows ? r : rows - 1;
+    const int64_t src = g.a_rows ? g.a_rows[row0 + r] : (int64_t)(row0 + r);
+    asrc[i] = g.A + src * K + 8 * ((lane & 7) ^ (lane >> 3));
+  }
+  int aoff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int c = 2 * s + h;
+    const int rr = r32 & 7;
+    aoff[s] = (r32 >> 3) * FRAG + (rr * 8 + (c ^ rr)) * 8;
+  }
+
+  // weight pointers of stage 0 and the byte offsets of a stage (bst) and of
+  // k-step q inside a stage (qoff)
+  const uint8_t *bptr[NB][NCB];
+  const bool tiled = g.tiled != 0;
+  const int64_t bst = tiled ? 2048 : BK * 2;
+  int qoff[KS];
+#pragma unroll
+  for (int q = 0; q < KS; ++q) qoff[q] = tiled ? (q >> 1) * 1024 + (q & 1) * 512 : 32 * q;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int64_t n = col0 + cb * 32 + r32;
+      const int64_t nb = n >> 4;               // 16-column block of this lane's column
+      const bf16 *base = t.shared ? g.SB[b] : (const bf16 *)g.B[b] + (int64_t)t.grp * N * K;
+      bptr[b][cb] = tiled ? (const uint8_t *)base + nb * (K / 32) * 1024 + ((r32 & 15) + 16 * h) * 16
+                          : (const uint8_t *)(base + n * K + h * 8);
+    }
+
+  f32x16 acc[M32][NB][NCB];
+#pragma unroll
+  for (int m = 0; m < M32; ++m)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[m][b][cb][e] = 0.f;
+
+  u32x4 bq[NS][NB][NCB][KS];             // weight operands
+  const int nst = K / BK;
+
+  auto issue_op = [&](int SL, int ST, int q) {
+    if (q < NFW) {
+      dma16(asrc[q] + (int64_t)ST * BK, As + SL * SLOT + (wave + WAVES * q) * FRAG);
+    } else {
+      const int r = q - NFW, bc = r / KS, qq = r - bc * KS, b = bc / NCB, cb = bc - b * NCB;
+      const u32x4 *src = (const u32x4 *)(bptr[b][cb] + ST * bst + qoff[qq]);
+      bq[SL][b][cb][qq] = SH ? *src : __builtin_nontemporal_load(src);
+    }
+  };
+  auto issue_stage = [&](int SL, int ST) {
+#pragma unroll
+    for (int q = 0; q < VM_PER_STAGE; ++q) issue_op(SL, ST, q);
+  };
+
+  const int last = nst - 1;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) issue_stage(p, p < last ? p : last);
+
+  // one stage from ring slot p, refilling the slot of stage st-1 with stage
+  // st+NS-1 between the MFMA chunks (as in gemm_tile).  The A operands of
+  // each chunk are read from LDS while the previous chunk's MFMAs run: with
+  // one wave per SIMD nothing else covers the LDS latency.
+  auto compute_stage = [&](int p, int st) {
+    const int nslot = (p + NS - 1) % NS;
+    const int nx = st + NS - 1 < last ? st + NS - 1 : last;
+    const bf16 *abase = As + p * SLOT;
+    auto read_a = [&](int s, int mc, bf16x8 *a) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        a[j] = *(const bf16x8 *)(abase + aoff[s] + (mc + j) * 4 * FRAG);
+    };
+    bf16x8 a[2][CH];
+    read_a(0, 0, a[0]);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int mc = 0; mc < M32; mc += CH) {
+        const int chunk = s * (M32 / CH) + mc / CH;
+        const int cur = chunk & 1;
+        // next chunk's A operands (none after the stage's last chunk)
+        if (chunk + 1 < NCHK) {
+          const int s1 = mc + CH < M32 ? s : s + 1;
+          const int mc1 = mc + CH < M32 ? mc + CH : 0;
+          read_a(s1, mc1, a[cur ^ 1]);
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              acc[mc + j][b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  a[cur][j], __builtin_bit_cast(bf16x8, bq[p][b][cb][s]), acc[mc + j][b][cb],
+                  0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < ISSUE_PER_CHUNK; ++j) {
+          const int q = chunk * ISSUE_PER_CHUNK + j;
+          if (q < VM_PER_STAGE) issue_op(nslot, nx, q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  const int nfull = nst - nst % NS;
+  for (int s0 = 0; s0 < nfull; s0 += NS) {
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT((NS - 2) * VM_PER_STAGE));
+      __builtin_amdgcn_s_barrier();
+      compute_stage(p, s0 + p);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) {
+    if (nfull + p < nst) {
+      __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+      __builtin_amdgcn_s_barrier();
+      compute_stage(p, nfull + p);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+
+  const float L = g.limit;
+  // epilogue: bf16 rows staged through the ring as in gemm_tile (32-row
+  // chunks; lane r32 writes column r32 of its block, the two lane halves
+  // rows 4 apart, which the 16-byte row pad puts on distinct banks)
+  constexpr int SW = WAVES * NCB * 32;
+  constexpr int STRIDE = SW + 8;
+  constexpr int RC0 = LDSE / STRIDE / 32 * 32;
+  constexpr int RC = RC0 < MBE * 16 ? RC0 : MBE * 16;
+  constexpr int NCHUNK = (MBE * 16 + RC - 1) / RC;
+  constexpr int CPR = SW / 8;
+  constexpr int NT = WAVES * 64;
+  constexpr int ITER = (RC * CPR + NT - 1) / NT;
+  static_assert(RC >= 32 && RC % 32 == 0, "ring holds at least one 32-row block");
+  const int slab0 = col0 - wave * NCB * 32;
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NCHUNK; ++c) {
+#pragma unroll
+    for (int m = c * RC / 32; m < (c + 1) * RC / 32 && m < M32; ++m)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        bf16 *srow = As + (row - c * RC) * STRIDE + wave * NCB * 32 + r32;
+        if constexpr (NB == 2) {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            srow[cb * 32] = (bf16)swiglu_pair(acc[m][0][cb][e], acc[m][1][cb][e], L);
+        } else {
+          // rows of block m lie in [32m, 32m + 32): row / 64 = m / 2 for every lane
+          const float w = __shfl(my_w[m >> 1], row & 63);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) srow[cb * 32] = (bf16)(acc[m][0][cb][e] * w);
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int idx = it * NT + (int)threadIdx.x;
+      const int rl = idx / CPR, pc = idx - rl * CPR;
+      const int row = c * RC + rl;
+      if (idx < RC * CPR && row < rows)
+        *(u32x4 *)(g.C + (int64_t)(row0 + row) * N + slab0 + pc * 8) =
+            *(const u32x4 *)(As + rl * STRIDE + pc * 8);
+    }
+    if (c + 1 < NCHUNK) __syncthreads();
+  }
+}
+
 template <int WAVES, int NB, int NCB, int MB, bool FP4, int NS>
 constexpr int gemm_slot_elems() {
   constexpr int SUBS = 2;
@@ -416,6 +648,52 @@ void grouped_gemm(const GemmArgs g) {
       gemm_tile<WAVES, NB, NCB, (MB < 14 ? MB : 14), FP4, NS, SLOT>(g, t, As);
     else
       gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT>(g, t, As);
+  }
+}
+
+// The 32x32x16 grouped GEMM: as grouped_gemm, with tile bodies of 2, 4, 6,
+// ... 16-row blocks.  Workgroups whose accumulators and weight ring take
+// more than 192 of a lane's registers run one wave per SIMD (512 registers).
+template <int WAVES, int NB, int NCB, int MB, int NS>
+constexpr int gemm32_waves_per_simd() {
+  return WAVES >= 8 ? 2 : ((MB / 2) * NB * NCB * 16 + NS * NB * NCB * 16 > 192 ? 1 : 2);
+}
+
+template <int WAVES, int NB, int NCB, int MB, int NS>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(gemm32_waves_per_simd<WAVES, NB, NCB, MB, NS>(),
+                                   gemm32_waves_per_simd<WAVES, NB, NCB, MB, NS>())))
+void grouped_gemm32(const GemmArgs g) {
+  constexpr int SLOT = gemm_slot_elems<WAVES, NB, NCB, MB, false, NS>();
+  // the copy ring, and at least 32 staged output rows for the epilogue
+  constexpr int EPI = 32 * (WAVES * NCB * 32 + 8);
+  constexpr int LDSE = NS * SLOT > EPI ? NS * SLOT : EPI;
+  __shared__ __attribute__((aligned(1024))) bf16 As[LDSE];
+  static_assert(MB % 2 == 0, "whole 32-row blocks");
+
+  int tile, slab;
+  if (!gemm_work_item(g, &tile, &slab)) return;
+  const TileCtx t = gemm_tile_ctx(g, tile, slab, WAVES, NCB * 32);
+  const int n2 = ((t.rows + 15) >> 4) + 1 & ~1;   // row blocks rounded up to even
+
+  if (t.shared || t.reread) {
+    gemm_tile32<WAVES, NB, NCB, MB, NS, SLOT, LDSE, true>(g, t, As);
+  } else if (n2 <= 2 || MB <= 2) {
+    gemm_tile32<WAVES, NB, NCB, 2, NS, SLOT, LDSE>(g, t, As);
+  } else if (n2 <= 4 || MB <= 4) {
+    gemm_tile32<WAVES, NB, NCB, (MB < 4 ? MB : 4), NS, SLOT, LDSE>(g, t, As);
+  } else if (n2 <= 6 || MB <= 6) {
+    gemm_tile32<WAVES, NB, NCB, (MB < 6 ? MB : 6), NS, SLOT, LDSE>(g, t, As);
+  } else if (n2 <= 8 || MB <= 8) {
+    gemm_tile32<WAVES, NB, NCB, (MB < 8 ? MB : 8), NS, SLOT, LDSE>(g, t, As);
+  } else if (n2 <= 10 || MB <= 10) {
+    gemm_tile32<WAVES, NB, NCB, (MB < 10 ? MB : 10), NS, SLOT, LDSE>(g, t, As);
+  } else if (n2 <= 12 || MB <= 12) {
+    gemm_tile32<WAVES, NB, NCB, (MB < 12 ? MB : 12), NS, SLOT, LDSE>(g, t, As);
+  } else if (n2 <= 14 || MB <= 14) {
+    gemm_tile32<WAVES, NB, NCB, (MB < 14 ? MB : 14), NS, SLOT, LDSE>(g, t, As);
+  } else {
+    gemm_tile32<WAVES, NB, NCB, MB, NS, SLOT, LDSE>(g, t, As);
   }
 }
 
@@ -581,6 +859,38 @@ static hipError_t run_gemm(const GemmArgs &a, int max_tiles, hipStream_t s) {
 // V4.1-Flash shapes; the first entry whose column slab divides N is used.
 struct GemmCfg { int waves, ncb, ns; };
 
+// The 32x32x16 kernel (NCB in 32-column blocks): fits when the in-flight
+// vector memory ops fit vmcnt and the copy ring the LDS.
+template <int WAVES, int NB, int NCB, int MB, int NS>
+constexpr bool gemm32_cfg_fits() {
+  constexpr int NFW = (MB * 2 + WAVES - 1) / WAVES;
+  constexpr int NBV = NB * NCB * 4;
+  return MB % 2 == 0 && (NS - 2) * (NFW + NBV) <= 63 && NS * NFW * WAVES * 1024 <= 160 * 1024;
+}
+
+template <int WAVES, int NB, int NCB, int MB, int NS>
+static hipError_t run_gemm32(const GemmArgs &a, int max_tiles, hipStream_t s) {
+  if constexpr (!gemm32_cfg_fits<WAVES, NB, NCB, MB, NS>()) {
+    return hipErrorInvalidValue;
+  } else {
+    const int64_t blocks = gemm_grid_blocks(a, max_tiles);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((grouped_gemm32<WAVES, NB, NCB, MB, NS>), dim3((unsigned)blocks),
+                       dim3(WAVES * 64), 0, s, a);
+    return hipGetLastError();
+  }
+}
+
+template <int WAVES, int NB, int NCB, int NS>
+static hipError_t run_gemm32_mb(int mb, const GemmArgs &a, int max_tiles, hipStream_t s) {
+  switch (mb) {
+    case 4: return run_gemm32<WAVES, NB, NCB, 4, NS>(a, max_tiles, s);
+    case 8: return run_gemm32<WAVES, NB, NCB, 8, NS>(a, max_tiles, s);
+    case 12: return run_gemm32<WAVES, NB, NCB, 12, NS>(a, max_tiles, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int WAVES, int NB, int NCB, bool FP4, int NS>
 static hipError_t run_gemm_mb(int mb, const GemmArgs &a, int max_tiles, hipStream_t s) {
   switch (mb) {
@@ -609,6 +919,20 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
     a.n_slabs = a.N / ((W) * (NCB) * 16);                                       \
     return run_gemm<W, NB_, NCB, 1, FP4_, NS>(a, max_tiles, s);                 \
   }
+#define MOE_TRY32(W, NB_, NCB, NS)                                              \
+  if (a.N % ((W) * (NCB) * 32) == 0) {                                          \
+    a.n_slabs = a.N / ((W) * (NCB) * 32);                                       \
+    return run_gemm32_mb<W, NB_, NCB, NS>(mb, a, max_tiles, s);                 \
+  }
+  // bf16 down GEMM on tiles of up to 192 rows: the 32x32x16 kernel (V3
+  // prefill shape 1.65 -> 1.58 ms, same-box A/B).  Elsewhere it measured
+  // level or slower than gemm_tile at the same slabs (hash and 2-gram
+  // layers, FP4 down GEMM 3-7 % slower; V3 and FP4 gate|up within 1 %), and
+  // so did 8-wave forms at two waves per SIMD (down GEMM one 32-column
+  // block per wave; gate|up with the waves split between W_gate and W_up).
+  if (!decode && a.Cf == nullptr && nb == 1 && !fp4 && mb <= 12) {
+    MOE_TRY32(4, 1, 2, 3)
+  }
   if (nb == 2) {
     if (fp4) {
       if (decode) { MOE_TRY_DECODE(4, 2, 2, true, 4) }
@@ -633,6 +957,7 @@ static hipError_t gemm_launch(int nb, bool fp4, int mb, GemmArgs a, int max_tile
   }
 #undef MOE_TRY
 #undef MOE_TRY_DECODE
+#undef MOE_TRY32
   return hipErrorInvalidValue;
 }
 
