@@ -115,20 +115,24 @@ def achievable_peaks(torch, B):
     torch.cuda.synchronize()
     read_gbs = 5 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
     rates = {}
-    for shape, name in ((0, "16x16x32"), (1, "32x32x16")):
+    for shape, name, iters in ((0, "16x16x32", 20000), (1, "32x32x16", 10000),
+                               (2, "fp8xfp4 16x16x128", 2500), (3, "fp8xfp8 16x16x128", 2500)):
+        B.moe_probe_mfma(10, out, shape)
         e0.record()
         flops = 0.0
         for _ in range(5):
-            flops += B.moe_probe_mfma(20000 if shape == 0 else 10000, out, shape)
+            flops += B.moe_probe_mfma(iters, out, shape)
         e1.record()
         torch.cuda.synchronize()
         rates[name] = round(flops / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
-    mfma_tflops = max(rates.values())
     del buf, out
     torch.cuda.empty_cache()
-    return {"hbm_read_gbs": round(read_gbs, 1), "bf16_mfma_tflops": mfma_tflops,
-            "bf16_mfma_tflops_by_shape": rates,
-            "how": "moe_probe_read over 4 GiB; moe_probe_mfma (2048 x 4 waves x 8 chains)"}
+    return {"hbm_read_gbs": round(read_gbs, 1),
+            "bf16_mfma_tflops": max(rates["16x16x32"], rates["32x32x16"]),
+            "fp8_mfma_tflops": max(rates["fp8xfp4 16x16x128"], rates["fp8xfp8 16x16x128"]),
+            "mfma_tflops_by_shape": rates,
+            "how": "moe_probe_read over 4 GiB; moe_probe_mfma (2048 x 4 waves; 8 independent "
+                   "chains per wave for bf16, 16 for the scaled FP8 shapes)"}
 
 
 def roofline_entry(flops, nbytes, seconds, peak_tflops):
@@ -573,6 +577,17 @@ def main():
         r = out["roofline"]
         denom = pk["hbm_read_gbs"] if r["unit"] == "GB/s" else pk["bf16_mfma_tflops"]
         r["frac_of_achievable"] = round(r["achieved"] / denom, 4)
+        for rep in [out.get("decode")] + list((out.get("extra_workloads") or {}).values()):
+            if not rep:
+                continue
+            rr = rep["roofline"]
+            if rr["unit"] == "GB/s":
+                rr["frac_of_achievable"] = round(rr["achieved"] / pk["hbm_read_gbs"], 4)
+            else:
+                key = {MFMA_PEAK_TFLOPS["fp8"]: "fp8_mfma_tflops",
+                       MFMA_PEAK_TFLOPS["bf16"]: "bf16_mfma_tflops"}.get(rr["peak"])
+                if key:
+                    rr["frac_of_achievable"] = round(rr["achieved"] / pk[key], 4)
         log(f"achievable: {pk}")
     if not args.no_peaks:
         log("timing the auxiliary calls")

@@ -197,7 +197,8 @@ def moe_probe_read(buf, out, stream=None):
 
 
 def moe_probe_mfma(iters: int, out, shape=0, stream=None) -> float:
-    """Launch the MFMA probe (shape 0: 16x16x32, 1: 32x32x16); returns the
+    """Launch the MFMA probe (shape 0: 16x16x32 bf16, 1: 32x32x16 bf16,
+    2: scaled 16x16x128 E4M3 x E2M1, 3: the same E4M3 x E4M3); returns the
     flops the launch performs."""
     flops = ctypes.c_double()
     _check(_lib.moe_probe_mfma(iters, shape, _ptr(out), ctypes.byref(flops), _stream(stream)),

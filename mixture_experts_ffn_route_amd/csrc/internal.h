@@ -120,7 +120,7 @@ hipError_t launch_pack_matrix(const void *src, void *dst, int64_t count, int64_t
 
 // Roofline probes (moe_probe_read / moe_probe_mfma).
 hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *out, hipStream_t s);
-hipError_t launch_probe_mfma(int iters, bool big, float *out, hipStream_t s);
-int64_t probe_mfma_flops(int iters, bool big);
+hipError_t launch_probe_mfma(int iters, int shape, float *out, hipStream_t s);
+int64_t probe_mfma_flops(int iters, int shape);
 
 }  // namespace moe

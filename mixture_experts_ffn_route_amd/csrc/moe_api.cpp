@@ -660,9 +660,9 @@ int moe_probe_read(const void *buf, int64_t bytes, void *out, void *stream) {
 }
 
 int moe_probe_mfma(int32_t iters, int32_t shape, void *out, double *flops, void *stream) {
-  if (!out || iters < 1 || (shape != 0 && shape != 1)) return MOE_ERR_INVALID_ARG;
-  if (flops) *flops = (double)moe::probe_mfma_flops(iters, shape == 1);
-  return hip_status(moe::launch_probe_mfma(iters, shape == 1, (float *)out, (hipStream_t)stream));
+  if (!out || iters < 1 || shape < 0 || shape > 3) return MOE_ERR_INVALID_ARG;
+  if (flops) *flops = (double)moe::probe_mfma_flops(iters, shape);
+  return hip_status(moe::launch_probe_mfma(iters, shape, (float *)out, (hipStream_t)stream));
 }
 
 }  // extern "C"

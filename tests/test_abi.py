@@ -259,7 +259,8 @@ def test_probes_check_before_any_launch():
     assert B._lib.moe_probe_read(fake, 8, fake, None) == B.MOE_ERR_INVALID_ARG
     assert B._lib.moe_probe_read(ctypes.c_void_p(0x100004), 1 << 20, fake, None) == B.MOE_ERR_INVALID_ARG
     assert B._lib.moe_probe_mfma(0, 0, fake, None, None) == B.MOE_ERR_INVALID_ARG
-    assert B._lib.moe_probe_mfma(10, 2, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert B._lib.moe_probe_mfma(10, 4, fake, None, None) == B.MOE_ERR_INVALID_ARG
+    assert B._lib.moe_probe_mfma(10, -1, fake, None, None) == B.MOE_ERR_INVALID_ARG
     assert B._lib.moe_probe_mfma(10, 0, None, None, None) == B.MOE_ERR_INVALID_ARG
 
 
