@@ -163,7 +163,8 @@ typedef struct {
   size_t flags;                /* uint32 [4]     device error flags (below)      */
   size_t route_logits;         /* float          partial gate logits (learned
                                   bf16 routing; 0 bytes otherwise)               */
-  size_t perm_hist;            /* int32          per-chunk expert histograms     */
+  size_t perm_hist;            /* int32          per-chunk expert histograms and
+                                  per-expert totals                          */
   size_t xq;                   /* uint8 [T, dim] MXFP8 codes of x (act_quant)   */
   size_t xq_scales;            /* uint8 [T, dim/32] their E8M0 scales            */
   size_t hq;                   /* uint8 [T*k, I] MXFP8 codes of H's routed rows  */

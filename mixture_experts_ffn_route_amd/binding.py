@@ -385,7 +385,7 @@ def workspace_views(cfg: MoEConfig, T: int, ws):
         "tiles": view(lay["tiles"], 4 * lay["max_tiles"], torch.int32).view(-1, 4),
         "tile_count": view(lay["tile_count"], 1, torch.int32),
         "flags": view(lay["flags"], 4, torch.int32),
-        "perm_hist": view(lay["perm_hist"], -(-T * k // 256) * E, torch.int32),
+        "perm_hist": view(lay["perm_hist"], (-(-T * k // 256) + 1) * E, torch.int32),
         "h": view(lay["h"], rows * cfg.moe_inter_dim, edt).view(rows, cfg.moe_inter_dim),
         "yrows": view(lay["yrows"], rows * cfg.dim, edt).view(rows, cfg.dim),
         "layout": lay,

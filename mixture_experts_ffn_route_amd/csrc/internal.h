@@ -57,8 +57,9 @@ struct TileSpec {
   float *sorted_w;           // [T*k]  gate value of each permuted row, or null
 };
 
-// chunk_hist: null (one workgroup) or int32 [permute_chunks(T*k) * E] of
-// workspace, which lets large batches use the many-workgroup kernels.
+// chunk_hist: null (one workgroup) or int32 [(permute_chunks(T*k) + 1) * E]
+// of workspace (per-chunk histograms, then per-expert totals), which lets
+// large batches use the many-workgroup kernels.
 hipError_t launch_permute(int E, int k, int64_t T, const int32_t *indices, int32_t *counts,
                           int32_t *offsets, int32_t *sorted_tok, int32_t *sorted_slot,
                           int32_t *inverse, uint32_t *flags, const TileSpec *tiles,

@@ -116,7 +116,7 @@ int make_layout(const moe_config *c, int64_t T, moe_ws_layout *out) {
   l.tile_count = take(sizeof(int32_t));
   l.flags = take(sizeof(uint32_t) * 4);
   l.route_logits = take(sizeof(float) * moe::route_logits_floats(*c, T));
-  l.perm_hist = take(sizeof(int32_t) * moe::permute_chunks(T * k) * E);
+  l.perm_hist = take(sizeof(int32_t) * (moe::permute_chunks(T * k) + 1) * E);
   const bool mx = c->act_quant == MOE_ACT_QUANT_MXFP8;
   l.xq = take(mx ? (size_t)T * c->dim : 0);
   l.xq_scales = take(mx ? (size_t)T * c->dim / 32 : 0);

@@ -169,7 +169,7 @@ def test_workspace_layout_is_aligned_and_disjoint():
                  # at least one partial-logit plane for the split bf16 router
                  "route_logits": 4 * T * E if (cfg.route_mode == "learned"
                                                and cfg.act_dtype == "bf16") else 0,
-                 "perm_hist": 4 * (-(-T * k // 256)) * E}
+                 "perm_hist": 4 * (-(-T * k // 256) + 1) * E}
         spans = sorted((lay[n], lay[n] + s) for n, s in sizes.items())
         for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
             assert a1 <= b0
