@@ -119,6 +119,42 @@ def test_permute_drops_out_of_range_ids(gpu):
     assert int(flags[0]) & B.MOE_FLAG_EXPERT_RANGE
 
 
+@pytest.mark.parametrize("E,k,T", [(6, 2, 2600), (13, 3, 2000), (64, 4, 1500)])
+def test_forward_chunked_permutation(E, k, T, gpu):
+    """Batches of more than 16 chunks of 256 pairs take the many-workgroup
+    permutation inside moe_forward (per-chunk histograms, one scan wave per
+    expert, the tile list from the expert totals); expert counts that are
+    not multiples of 4 or 8 exercise the ragged ends of the per-expert and
+    per-XCD splits.  Permutation bit-exact, tile list covering every expert's
+    rows once, layer output against the oracle."""
+    base = C.SMALL_WORKLOADS["hash_small"]
+    wl = replace(base, name=f"hash_chunked_e{E}", T=T,
+                 cfg=replace(base.cfg, n_routed_experts=E, n_activated_experts=k))
+    cfg = wl.cfg
+    assert T * k > 16 * 256
+    layer, ora_table = _layer(wl, gpu)
+    y, ws = _forward(wl, layer, gpu)
+    v = B.workspace_views(cfg, T, ws)
+    ow, oidx, aux = H.oracle_route(cfg, layer, ora_table)
+    rc = H.check_routing(cfg, H.cpu_np(v["route_weights"]), H.cpu_np(v["route_indices"]),
+                         ow, oidx, aux, label=wl.name)
+    counts, offsets = H.cpu_np(v["counts"]), H.cpu_np(v["offsets"])
+    st, ss, inv = H.cpu_np(v["sorted_tok"]), H.cpu_np(v["sorted_slot"]), H.cpu_np(v["inverse"])
+    H.check_permutation_exact(rc.idx, E, counts, offsets, st, ss, inv)
+    n = int(v["tile_count"][0])
+    covered = np.zeros(E + 1, dtype=np.int64)
+    for grp, row0, rows, _ in H.cpu_np(v["tiles"])[:n]:
+        assert rows > 0 and 0 <= grp <= E
+        if grp < E:
+            assert offsets[grp] <= row0 and row0 + rows <= offsets[grp + 1]
+        covered[grp] += rows
+    np.testing.assert_array_equal(covered[:E], counts)
+    assert covered[E] == T
+    yref = H.oracle_forward(cfg, H.f64(layer["x"]), rc.ref_w, rc.idx, layer)
+    H.check_layer_output(cfg, H.f64(y), yref, label=wl.name)
+    assert int(v["flags"][0]) == 0
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_forward_small(name, gpu):
     wl = C.SMALL_WORKLOADS[name]
