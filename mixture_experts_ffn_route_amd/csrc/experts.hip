@@ -640,10 +640,18 @@ void grouped_gemm(const GemmArgs g) {
     gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT>(g, t, As);
   } else if (!FP4 && (t.shared || t.reread)) {
     // tiles whose weights other tiles stream too (an expert of several tiles,
-    // the shared expert, the dense form): plain weight loads (see above);
-    // such tiles are full height but for the last, so one body of MB blocks
-    // serves them
-    gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT, true>(g, t, As);
+    // the shared expert, the dense form): plain weight loads (see above).
+    // Such tiles are full height but for the last, which is often a short
+    // remainder (the hash layers' 257-276-row experts leave 1-20 rows after
+    // a 256-row tile): it takes a 4- or 8-block body, not MB blocks of MFMAs
+    // on padding rows.
+    const int n2 = (nmb + 1) / 2 * 2;
+    if (MB > 4 && n2 <= 4)
+      gemm_tile<WAVES, NB, NCB, (MB > 4 ? 4 : MB), FP4, NS, SLOT, true>(g, t, As);
+    else if (MB > 8 && n2 <= 8)
+      gemm_tile<WAVES, NB, NCB, (MB > 8 ? 8 : MB), FP4, NS, SLOT, true>(g, t, As);
+    else
+      gemm_tile<WAVES, NB, NCB, MB, FP4, NS, SLOT, true>(g, t, As);
   } else {
     const int n2 = (nmb + 1) / 2 * 2;
     if (n2 <= 4 || MB <= 4)
@@ -689,7 +697,13 @@ void grouped_gemm32(const GemmArgs g) {
   const int n2 = ((t.rows + 15) >> 4) + 1 & ~1;   // row blocks rounded up to even
 
   if (t.shared || t.reread) {
-    gemm_tile32<WAVES, NB, NCB, MB, NS, SLOT, LDSE, true>(g, t, As);
+    // plain weight loads; a short last tile takes a short body (as above)
+    if (MB > 4 && n2 <= 4)
+      gemm_tile32<WAVES, NB, NCB, (MB > 4 ? 4 : MB), NS, SLOT, LDSE, true>(g, t, As);
+    else if (MB > 8 && n2 <= 8)
+      gemm_tile32<WAVES, NB, NCB, (MB > 8 ? 8 : MB), NS, SLOT, LDSE, true>(g, t, As);
+    else
+      gemm_tile32<WAVES, NB, NCB, MB, NS, SLOT, LDSE, true>(g, t, As);
   } else if (n2 <= 2 || MB <= 2) {
     gemm_tile32<WAVES, NB, NCB, 2, NS, SLOT, LDSE>(g, t, As);
   } else if (n2 <= 4 || MB <= 4) {
