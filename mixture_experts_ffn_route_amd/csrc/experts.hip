@@ -642,9 +642,9 @@ void grouped_gemm(const GemmArgs g) {
     // tiles whose weights other tiles stream too (an expert of several tiles,
     // the shared expert, the dense form): plain weight loads (see above).
     // Such tiles are full height but for the last, which is often a short
-    // remainder (the hash layers' 257-276-row experts leave 1-20 rows after
-    // a 256-row tile): it takes a 4- or 8-block body, not MB blocks of MFMAs
-    // on padding rows.
+    // remainder (an expert of 600 rows in 256-row tiles leaves 88, the
+    // shared expert's 4096 rows in 192-row tiles leave 64): it takes a 4- or
+    // 8-block body, not MB blocks of MFMAs on padding rows.
     const int n2 = (nmb + 1) / 2 * 2;
     if (MB > 4 && n2 <= 4)
       gemm_tile<WAVES, NB, NCB, (MB > 4 ? 4 : MB), FP4, NS, SLOT, true>(g, t, As);
